@@ -1,0 +1,167 @@
+/*
+ * pa.h - C ABI of the paged-attention hot path for MI355X (gfx950).
+ *
+ * The operations come from the pages "Inside vLLM: Anatomy of a
+ * High-Throughput LLM Inference System" (bilingual copy at s.sunxiunan.com,
+ * Chinese translation at uml.org.cn, part-2 copy on the chengshu blog):
+ *
+ *   - the KV cache is carved into blocks of 16 tokens (section "Scheduler");
+ *     one block of one standard layer holds 2 * block_size * num_kv_heads *
+ *     head_size * dtype_bytes bytes (uml.org.cn, section "LLM Engine 构造函数");
+ *   - each step builds block tables and a slot_mapping, flattens all
+ *     sequences into one super sequence, and runs paged attention in which
+ *     positions and masks keep every sequence to its own tokens (section
+ *     "Run forward pass");
+ *   - the forward pass writes the new tokens' keys and values into the paged
+ *     KV memory (section "Prefix Caching"), and one step may hold decode rows
+ *     and chunks of long prompts side by side (sections "Scheduler" and
+ *     "Chunked prefill").
+ *
+ * Conventions for every entry point:
+ *   - Tensors are row-major and contiguous; "device" pointers point to HIP
+ *     device memory of the current device; element type bf16 unless stated.
+ *   - The caller owns every buffer, including the workspace. The library
+ *     keeps no pointer after a call returns and allocates nothing on the hot
+ *     path (pa_cache_write, pa_forward).
+ *   - pa_cache_write and pa_forward only enqueue work on `stream` (a
+ *     hipStream_t; NULL = the null stream) and return: no device-to-host
+ *     copy, no synchronisation. Call pa_cache_write for a step's tokens
+ *     before pa_forward on the same stream.
+ *   - Host-known arguments are checked before anything is launched; a
+ *     negative pa_status is returned and pa_last_error() describes it.
+ *     Device-resident metadata (slots, lengths, tables) is trusted on the hot
+ *     path; pa_validate_inputs checks it synchronously.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,         /* a required pointer is NULL                          */
+  PA_ERR_SHAPE = -2,        /* a size is out of range or sizes disagree            */
+  PA_ERR_UNSUPPORTED = -3,  /* valid but not built: head_size, group size, block   */
+  PA_ERR_ALIGN = -4,        /* a pointer is not 16-byte aligned                    */
+  PA_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required          */
+  PA_ERR_HIP = -6,          /* a HIP runtime call or kernel launch failed          */
+  PA_ERR_INVALID_DATA = -7  /* pa_validate_inputs found inconsistent metadata      */
+} pa_status;
+
+/* Tokens per KV-cache block; the only block size the kernels accept. */
+#define PA_BLOCK_SIZE 16
+
+/*
+ * Bytes of one KV-cache block of one layer (key and value together):
+ * 2 * block_size * num_kv_heads * head_size * dtype_bytes
+ * (uml.org.cn translation, section "LLM Engine 构造函数"). Pure host
+ * arithmetic; returns -1 if an argument is not positive.
+ */
+int64_t pa_kv_block_bytes(int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                          int32_t dtype_bytes);
+
+/*
+ * KV-cache write (section "Run forward pass": slot_mapping; section "Prefix
+ * Caching": the forward pass populates the allocated blocks).
+ *
+ *   k, v          device, bf16 [num_tokens, num_kv_heads, head_size]
+ *   slot_mapping  device, int64 [num_tokens]; token t goes to row
+ *                 slot % block_size of block slot / block_size; slot < 0
+ *                 skips the token (padding)
+ *   k_cache,      device, bf16 [num_blocks, block_size, num_kv_heads,
+ *   v_cache       head_size], written in place
+ *
+ * The copy is bit-exact. Caller contract (not checked on this path): every
+ * slot is < num_blocks * block_size and no two tokens share a slot.
+ * num_tokens == 0 is a no-op. Requires block_size == 16, head_size a multiple
+ * of 8, 16-byte aligned k, v, k_cache, v_cache.
+ */
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                   int64_t num_blocks, int32_t block_size, void* stream);
+
+/*
+ * Workspace bytes pa_forward needs for these sizes (the split-K partial
+ * results of decode rows and the work list of prefill tiles). Depends only
+ * on its arguments; returns 0 if an argument is out of range.
+ * max_seq_len_hint <= 0 means "unknown" (max_blocks_per_seq * 16 is used).
+ */
+size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_size,
+                                  int32_t max_blocks_per_seq, int32_t max_seq_len_hint);
+
+/*
+ * Paged attention over a flattened varlen batch (section "Run forward pass",
+ * step 3; chunked rows per section "Chunked prefill").
+ *
+ *   q                device, bf16 [num_tokens, num_q_heads, head_size]
+ *   k_cache, v_cache device, bf16 [num_blocks, 16, num_kv_heads, head_size]
+ *   block_table      device, int32 [num_seqs, max_blocks_per_seq]; only the
+ *                    first ceil(seq_lens[s] / 16) entries of row s are read
+ *   seq_lens         device, int32 [num_seqs]: tokens in the cache for
+ *                    sequence s after this step's write (context + new)
+ *   query_start_loc  device, int32 [num_seqs + 1]: exclusive prefix sum of
+ *                    the per-sequence query counts; [0] = 0, [S] = num_tokens
+ *   scale            softmax scale applied to q.k (e.g. 1/sqrt(head_size))
+ *   out              device, bf16 [num_tokens, num_q_heads, head_size]
+ *   max_query_len_hint, max_seq_len_hint
+ *                    host upper bounds of q_len and seq_len over the batch;
+ *                    <= 0 = unknown (num_tokens and max_blocks_per_seq * 16
+ *                    are used). A hint below the true maximum is a contract
+ *                    violation (rows past it are not computed).
+ *   workspace        device, >= pa_forward_workspace_bytes(...) bytes, 256-
+ *                    byte aligned; contents need no initialisation and are
+ *                    scratch after the call. Calls that share a workspace
+ *                    must be ordered on one stream.
+ *
+ * Query row i of sequence s (i < q_len = qsl[s+1] - qsl[s]) sits at position
+ * c + i with c = seq_lens[s] - q_len and attends to keys 0..c+i of its own
+ * sequence; query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Rows with q_len == 0 produce nothing; rows with q_len == 1 take the decode
+ * path (split-K over the context), rows with q_len > 1 the prefill path.
+ * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
+ * Requires block_size == 16, head_size in {64, 128}, num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8, 16}. Caller contract: 0 <= q_len <= seq_len
+ * <= max_blocks_per_seq * 16 and the first ceil(seq_len / 16) table entries
+ * of each row are valid block ids.
+ */
+int pa_forward(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens,
+               const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
+               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+               int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+               int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronous check of the device-resident metadata that the hot path
+ * trusts (for tests and debugging; copies to the host and waits on
+ * `stream`). Checks: query_start_loc starts at 0, never decreases and ends at
+ * num_tokens; 0 <= q_len <= seq_len <= max_blocks_per_seq * 16; the table
+ * entries a row reads are in [0, num_blocks); hints, when given, bound the
+ * true maxima; and, if slot_mapping is not NULL, every slot of its
+ * num_write_tokens entries is < num_blocks * 16 and no slot repeats.
+ * Returns PA_OK or PA_ERR_INVALID_DATA (or an argument error).
+ */
+int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, const int64_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                       int64_t num_blocks, int32_t block_size, int32_t num_write_tokens,
+                       int32_t max_query_len_hint, int32_t max_seq_len_hint, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,213 @@
+"""Paged attention and paged KV-cache write for MI355X (gfx950).
+
+Python binding of ``libpa.so`` (the C ABI declared in ``include/pa.h``). The
+binding only marshals arguments: it reads sizes from tensor shapes, passes
+``data_ptr()`` values and the current HIP stream, and raises on a non-zero
+status. Every step of the computation runs in the library's HIP kernels;
+there is no fallback path, and importing a function that needs the library
+raises if ``libpa.so`` has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["cache_write", "forward", "forward_workspace_bytes", "validate_inputs",
+           "kv_block_bytes", "last_error", "version", "library_path", "load_library",
+           "PaError", "BLOCK_SIZE"]
+
+BLOCK_SIZE = 16
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpa.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
+          -4: "PA_ERR_ALIGN", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP",
+          -7: "PA_ERR_INVALID_DATA"}
+
+# (name, restype, argtypes) of every symbol include/pa.h declares.
+SIGNATURES = {
+    "pa_kv_block_bytes": (_I64, [_I32, _I32, _I32, _I32]),
+    "pa_cache_write": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P]),
+    "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32,
+                                  _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
+    "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
+                                          _I32, _I32, _P]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_char_p, []),
+}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpa.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m paged_attention_kv_amd.build` "
+                "(the paged-attention path has no fallback)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return load_library().pa_last_error().decode()
+
+
+def version() -> str:
+    return load_library().pa_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PaError(status, last_error())
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, not {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, has {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def kv_block_bytes(block_size: int, num_kv_heads: int, head_size: int, dtype_bytes: int) -> int:
+    return int(load_library().pa_kv_block_bytes(block_size, num_kv_heads, head_size, dtype_bytes))
+
+
+def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Write this step's keys/values ([T, Hkv, D] bf16) into the paged caches
+    ([NB, 16, Hkv, D] bf16) at ``slot_mapping`` (int64 [T], negative = skip)."""
+    lib = load_library()
+    for n, t in (("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(n, t, torch.bfloat16, 4)
+    _dev_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+    T, Hkv, D = k.shape
+    if v.shape != k.shape or slot_mapping.shape[0] != T:
+        raise ValueError("k, v and slot_mapping disagree in shape")
+    if k_cache.shape != v_cache.shape or tuple(k_cache.shape[2:]) != (Hkv, D):
+        raise ValueError("cache shape must be [NB, 16, Hkv, D] matching k")
+    _check(lib.pa_cache_write(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                              k_cache.data_ptr(), v_cache.data_ptr(), T, Hkv, D,
+                              k_cache.shape[0], k_cache.shape[1], _stream(k_cache)))
+
+
+def forward_workspace_bytes(num_tokens: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                            head_size: int, max_blocks_per_seq: int,
+                            max_seq_len: Optional[int] = None) -> int:
+    n = load_library().pa_forward_workspace_bytes(num_tokens, num_seqs, num_q_heads, num_kv_heads,
+                                                  head_size, max_blocks_per_seq, max_seq_len or 0)
+    if n == 0:
+        raise ValueError("unsupported sizes for pa_forward")
+    return int(n)
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+            block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+            scale: float, out: Optional[torch.Tensor] = None,
+            max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
+            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
+    paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
+    ``max_seq_len`` are optional host upper bounds that shrink the launch
+    grids; ``workspace`` (uint8, on the device) is taken from a per-device
+    cache when omitted."""
+    lib = load_library()
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(n, t, torch.bfloat16, 4)
+    _dev_tensor("block_table", block_table, torch.int32, 2)
+    _dev_tensor("seq_lens", seq_lens, torch.int32, 1)
+    _dev_tensor("query_start_loc", query_start_loc, torch.int32, 1)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, Dc = k_cache.shape
+    S, MB = block_table.shape
+    if v_cache.shape != k_cache.shape or Dc != D:
+        raise ValueError("caches must be [NB, 16, Hkv, D] with q's head size")
+    if seq_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("seq_lens must be [S] and query_start_loc [S+1]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor("out", out, torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    need = lib.pa_forward_workspace_bytes(T, S, Hq, Hkv, D, MB, max_seq_len or 0)
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    elif workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
+    _check(lib.pa_forward(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                          block_table.data_ptr(), seq_lens.data_ptr(),
+                          query_start_loc.data_ptr(), float(scale), out.data_ptr(), T, S, Hq,
+                          Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream(q)))
+    return out
+
+
+def validate_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor,
+                    query_start_loc: torch.Tensor, num_tokens: int, num_blocks: int,
+                    slot_mapping: Optional[torch.Tensor] = None,
+                    max_query_len: Optional[int] = None,
+                    max_seq_len: Optional[int] = None) -> None:
+    """Synchronously check the device metadata the hot path trusts; raises
+    PaError(PA_ERR_INVALID_DATA) with the first problem found."""
+    lib = load_library()
+    S, MB = block_table.shape
+    nw = 0 if slot_mapping is None else slot_mapping.shape[0]
+    _check(lib.pa_validate_inputs(block_table.data_ptr(), seq_lens.data_ptr(),
+                                  query_start_loc.data_ptr(),
+                                  None if slot_mapping is None else slot_mapping.data_ptr(),
+                                  num_tokens, S, MB, num_blocks, BLOCK_SIZE, nw,
+                                  max_query_len or 0, max_seq_len or 0,
+                                  _stream(block_table)))

@@ -1,0 +1,300 @@
+// C ABI of the paged-attention library: argument checks, workspace planning
+// and kernel dispatch. Declarations and the contract of every entry point
+// are in include/pa.h.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "kernels.h"
+#include "pa.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int32_t kMinPartTokens = 128;
+constexpr int32_t kMaxPartTokens = 1024;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int32_t resolved_max_seq_len(int32_t max_blocks_per_seq, int32_t hint) {
+  const int32_t cap = max_blocks_per_seq * PA_BLOCK_SIZE;
+  return hint > 0 ? std::min(hint, cap) : cap;
+}
+
+// Tokens per split-K partition of a decode row: the largest size that still
+// yields at least two workgroups per CU of a 256-CU part when every row is as
+// long as the longest. PA_DECODE_PART_TOKENS overrides it (multiple of 16 in
+// [128, 1024]) for tuning sweeps.
+int32_t choose_part_tokens(int32_t num_seqs, int32_t max_len) {
+  static const int32_t env = [] {
+    const char* e = getenv("PA_DECODE_PART_TOKENS");
+    if (!e) return 0;
+    const int v = atoi(e);
+    return (v >= kMinPartTokens && v <= kMaxPartTokens && v % PA_BLOCK_SIZE == 0) ? v : 0;
+  }();
+  if (env) return env;
+  for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
+    const int64_t items = (int64_t)num_seqs * ((max_len + p - 1) / p);
+    if (items >= 512) return p;
+  }
+  return kMinPartTokens;
+}
+
+bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+}  // namespace
+
+namespace pa {
+
+bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,
+                    int32_t max_seq_len_hint, WorkspaceLayout* out) {
+  if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_size <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads)
+    return false;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!supported_group(group)) return false;
+  const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
+  WorkspaceLayout w;
+  w.part_tokens = choose_part_tokens(num_seqs, max_len);
+  // Reserve for the smallest partition size so any tuning choice fits.
+  w.num_parts_max = (max_len + kMinPartTokens - 1) / kMinPartTokens;
+  w.tile_queries = prefill_tile_queries(group);
+  w.tile_bound = (num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
+  const size_t rows = (size_t)num_seqs * w.num_parts_max * num_q_heads;
+  w.off_o = 0;
+  w.off_ml = round_up(w.off_o + rows * head_size * sizeof(float), kAlign);
+  w.off_tiles = round_up(w.off_ml + rows * 2 * sizeof(float), kAlign);
+  w.total = round_up(w.off_tiles + (size_t)w.tile_bound * 2 * sizeof(int32_t), kAlign);
+  *out = w;
+  return true;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+int64_t pa_kv_block_bytes(int32_t block_size, int32_t num_kv_heads, int32_t head_size,
+                          int32_t dtype_bytes) {
+  if (block_size <= 0 || num_kv_heads <= 0 || head_size <= 0 || dtype_bytes <= 0) return -1;
+  return (int64_t)2 * block_size * num_kv_heads * head_size * dtype_bytes;
+}
+
+int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                   void* v_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_size,
+                   int64_t num_blocks, int32_t block_size, void* stream) {
+  g_last_error.clear();
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "pa_cache_write: num_tokens=%d num_kv_heads=%d head_size=%d "
+                "num_blocks=%lld out of range", num_tokens, num_kv_heads, head_size,
+                (long long)num_blocks);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "pa_cache_write: block_size %d (only %d is built)",
+                block_size, PA_BLOCK_SIZE);
+  if (head_size % 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_cache_write: head_size %d is not a multiple of 8",
+                head_size);
+  if (!k_cache || !v_cache) return fail(PA_ERR_NULL, "pa_cache_write: null cache pointer");
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_NULL, "pa_cache_write: null k/v/slot_mapping");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return fail(PA_ERR_ALIGN, "pa_cache_write: k, v and caches must be 16-byte aligned");
+  hipError_t e = pa::launch_cache_write(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+                                        num_kv_heads, head_size, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pa_cache_write launch");
+  return PA_OK;
+}
+
+size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_size,
+                                  int32_t max_blocks_per_seq, int32_t max_seq_len_hint) {
+  pa::WorkspaceLayout w;
+  if (!pa::plan_workspace(num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
+                          max_blocks_per_seq, max_seq_len_hint, &w))
+    return 0;
+  return w.total;
+}
+
+int pa_forward(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens,
+               const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
+               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+               int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+               int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "pa_forward: a size is out of range (T=%d S=%d Hq=%d Hkv=%d D=%d "
+                "MB=%d NB=%lld)", num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
+                max_blocks_per_seq, (long long)num_blocks);
+  if (num_q_heads % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "pa_forward: num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (num_tokens > 0 && num_seqs == 0)
+    return fail(PA_ERR_SHAPE, "pa_forward: %d tokens but no sequences", num_tokens);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: block_size %d (only %d is built)", block_size,
+                PA_BLOCK_SIZE);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: head_size %d (built: 64, 128)", head_size);
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!supported_group(group))
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: %d query heads per KV head (built: 1, 2, 4, 8, "
+                "16)", group);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(PA_ERR_SHAPE, "pa_forward: scale is not finite");
+  if (num_tokens == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
+    return fail(PA_ERR_NULL, "pa_forward: null pointer argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
+    return fail(PA_ERR_ALIGN, "pa_forward: q, caches and out must be 16-byte aligned");
+  pa::WorkspaceLayout w;
+  if (!pa::plan_workspace(num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
+                          max_blocks_per_seq, max_seq_len_hint, &w))
+    return fail(PA_ERR_SHAPE, "pa_forward: cannot plan the workspace");
+  if (!workspace || workspace_bytes < w.total)
+    return fail(PA_ERR_WORKSPACE, "pa_forward: workspace of %zu bytes, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, w.total);
+  if (!aligned(workspace, 16))
+    return fail(PA_ERR_ALIGN, "pa_forward: workspace must be 16-byte aligned");
+
+  pa::ForwardArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.out = out;
+  a.scale = scale;
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
+  a.max_query_len = max_query_len_hint > 0 ? std::min(max_query_len_hint, num_tokens)
+                                           : num_tokens;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  if (a.max_query_len > 1) {
+    pa::PrefillPlan pp;
+    pp.tile_queries = w.tile_queries;
+    const int64_t by_hint =
+        (int64_t)num_seqs * ((a.max_query_len + w.tile_queries - 1) / w.tile_queries);
+    pp.tile_bound = (int32_t)std::min<int64_t>(w.tile_bound, by_hint);
+    pp.tiles = (int32_t*)(ws + w.off_tiles);
+    hipError_t e = pa::launch_prefill(a, pp, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_forward prefill launch");
+  }
+  pa::DecodePlan dp;
+  dp.part_tokens = w.part_tokens;
+  dp.num_parts_max = (a.max_seq_len + w.part_tokens - 1) / w.part_tokens;
+  dp.ws_o = (float*)(ws + w.off_o);
+  dp.ws_ml = (float*)(ws + w.off_ml);
+  hipError_t e = pa::launch_decode(a, dp, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_forward decode launch");
+  return PA_OK;
+}
+
+int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, const int64_t* slot_mapping,
+                       int32_t num_tokens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                       int64_t num_blocks, int32_t block_size, int32_t num_write_tokens,
+                       int32_t max_query_len_hint, int32_t max_seq_len_hint, void* stream) {
+  g_last_error.clear();
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      num_write_tokens < 0)
+    return fail(PA_ERR_SHAPE, "pa_validate_inputs: a size is out of range");
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "pa_validate_inputs: block_size %d", block_size);
+  if (!block_table || !seq_lens || !query_start_loc || (num_write_tokens > 0 && !slot_mapping))
+    return fail(PA_ERR_NULL, "pa_validate_inputs: null pointer argument");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "pa_validate_inputs sync");
+  std::vector<int32_t> qsl(num_seqs + 1), lens(num_seqs),
+      table((size_t)num_seqs * max_blocks_per_seq);
+  std::vector<int64_t> slots(num_write_tokens);
+  if ((e = hipMemcpy(qsl.data(), query_start_loc, qsl.size() * 4, hipMemcpyDeviceToHost)) ||
+      (num_seqs && (e = hipMemcpy(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost))) ||
+      (num_seqs && (e = hipMemcpy(table.data(), block_table, table.size() * 4,
+                                  hipMemcpyDeviceToHost))) ||
+      (num_write_tokens && (e = hipMemcpy(slots.data(), slot_mapping, slots.size() * 8,
+                                          hipMemcpyDeviceToHost))))
+    return hip_fail(e, "pa_validate_inputs copy");
+  if (qsl[0] != 0) return fail(PA_ERR_INVALID_DATA, "query_start_loc[0] = %d, not 0", qsl[0]);
+  if (qsl[num_seqs] != num_tokens)
+    return fail(PA_ERR_INVALID_DATA, "query_start_loc[S] = %d, not num_tokens = %d",
+                qsl[num_seqs], num_tokens);
+  const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+  int32_t max_q = 0, max_l = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t ql = qsl[s + 1] - qsl[s];
+    if (ql < 0) return fail(PA_ERR_INVALID_DATA, "query_start_loc decreases at sequence %d", s);
+    if (lens[s] < ql || lens[s] > cap)
+      return fail(PA_ERR_INVALID_DATA, "sequence %d: seq_len %d outside [q_len %d, %lld]", s,
+                  lens[s], ql, (long long)cap);
+    max_q = std::max(max_q, ql);
+    max_l = std::max(max_l, lens[s]);
+    const int32_t nb = (lens[s] + block_size - 1) / block_size;
+    for (int32_t b = 0; b < nb; ++b) {
+      const int32_t id = table[(size_t)s * max_blocks_per_seq + b];
+      if (id < 0 || id >= num_blocks)
+        return fail(PA_ERR_INVALID_DATA, "sequence %d: block_table[%d] = %d outside [0, %lld)", s,
+                    b, id, (long long)num_blocks);
+    }
+  }
+  if (max_query_len_hint > 0 && max_query_len_hint < max_q)
+    return fail(PA_ERR_INVALID_DATA, "max_query_len_hint %d < longest query %d",
+                max_query_len_hint, max_q);
+  if (max_seq_len_hint > 0 && max_seq_len_hint < max_l)
+    return fail(PA_ERR_INVALID_DATA, "max_seq_len_hint %d < longest sequence %d",
+                max_seq_len_hint, max_l);
+  std::unordered_set<int64_t> seen;
+  for (int32_t t = 0; t < num_write_tokens; ++t) {
+    const int64_t sl = slots[t];
+    if (sl < 0) continue;
+    if (sl >= num_blocks * block_size)
+      return fail(PA_ERR_INVALID_DATA, "slot_mapping[%d] = %lld outside the pool", t,
+                  (long long)sl);
+    if (!seen.insert(sl).second)
+      return fail(PA_ERR_INVALID_DATA, "slot %lld is written twice", (long long)sl);
+  }
+  return PA_OK;
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+const char* pa_version(void) { return "paged_attention_kv_amd 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+"""The C ABI on the CPU: libpa.so loads, exports every symbol include/pa.h
+declares, and rejects bad host arguments before launching anything. No
+kernel runs here (no GPU), only host-side argument checks and pure host
+arithmetic."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import paged_attention_kv_amd as pa
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+NULL = None
+FAKE = 4096 * 16  # 16-byte aligned, never dereferenced: every call below fails before a launch
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(pa.SIGNATURES), "binding and header disagree"
+    raw = ctypes.CDLL(pa.library_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} not exported"
+
+
+def test_version(lib):
+    assert "gfx950" in pa.version()
+
+
+@pytest.mark.parametrize("hkv,d", [(4, 64), (8, 128), (1, 256), (2, 80)])
+def test_block_bytes_matches_oracle(lib, hkv, d):
+    assert pa.kv_block_bytes(16, hkv, d, 2) == oracle.kv_block_bytes(16, hkv, d, 2)
+    assert pa.kv_block_bytes(0, hkv, d, 2) == -1
+
+
+def cw(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, slot=FAKE, kc=FAKE, vc=FAKE, T=4, Hkv=4, D=64, NB=10, bs=16)
+    a.update(kw)
+    return lib.pa_cache_write(a["k"], a["v"], a["slot"], a["kc"], a["vc"], a["T"], a["Hkv"],
+                              a["D"], a["NB"], a["bs"], None)
+
+
+def test_cache_write_rejects_bad_arguments(lib):
+    assert cw(lib, kc=NULL) == -1
+    assert cw(lib, k=NULL) == -1
+    assert cw(lib, T=-1) == -2
+    assert cw(lib, Hkv=0) == -2
+    assert cw(lib, NB=0) == -2
+    assert cw(lib, bs=32) == -3
+    assert "block_size" in pa.last_error()
+    assert cw(lib, D=60) == -3
+    assert cw(lib, k=FAKE + 8) == -4
+    assert cw(lib, T=0) == 0          # nothing to write: no launch
+
+
+def fw(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, qsl=FAKE, scale=0.125, out=FAKE, T=8, S=2,
+             Hq=32, Hkv=4, D=64, bs=16, MB=4, NB=64, mq=0, ms=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.pa_forward(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["qsl"], a["scale"], a["out"],
+                          a["T"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"],
+                          a["mq"], a["ms"], a["ws"], a["wsb"], None)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    assert fw(lib, q=NULL) == -1
+    assert fw(lib, bt=NULL) == -1
+    assert fw(lib, Hq=30) == -2          # not a multiple of Hkv
+    assert fw(lib, S=0) == -2            # tokens without sequences
+    assert fw(lib, MB=0) == -2
+    assert fw(lib, D=96) == -3
+    assert fw(lib, bs=8) == -3
+    assert fw(lib, Hq=12, Hkv=4) == -3   # group of 3 is not built
+    assert fw(lib, scale=float("nan")) == -2
+    assert fw(lib, out=FAKE + 2) == -4
+    assert fw(lib, ws=NULL) == -5
+    assert fw(lib, wsb=16) == -5
+    assert "workspace" in pa.last_error()
+    assert fw(lib, T=0) == 0              # empty batch: no launch
+
+
+def test_validate_rejects_null_before_touching_the_device(lib):
+    assert lib.pa_validate_inputs(None, FAKE, FAKE, None, 4, 2, 4, 64, 16, 0, 0, 0, None) == -1
+    assert lib.pa_validate_inputs(FAKE, FAKE, FAKE, None, 4, 2, 4, 64, 16, 3, 0, 0, None) == -1
+    assert lib.pa_validate_inputs(FAKE, FAKE, FAKE, None, 4, 2, 4, 64, 8, 0, 0, 0, None) == -3
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_workspace_sizes_for_the_named_workloads(lib, i):
+    s = wl.config(i)
+    n = pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads, s.num_kv_heads,
+                                   s.head_size, s.max_blocks_per_seq)
+    # split-K partials of every row at the smallest partition (128 tokens)
+    parts = -(-s.max_blocks_per_seq * 16 // 128)
+    assert n >= s.num_seqs * parts * s.num_q_heads * (s.head_size + 2) * 4
+    assert n % 256 == 0
+    assert n < 512 << 20
+    # a tighter max_seq_len hint never needs more
+    n2 = pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads, s.num_kv_heads,
+                                    s.head_size, s.max_blocks_per_seq, max(s.seq_lens))
+    assert n2 <= n

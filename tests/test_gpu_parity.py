@@ -1,0 +1,303 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+KV write: bit-exact against oracle.ref_cache_write, and nothing else in the
+pool moves. Attention: max abs error <= 1e-2 and mean abs error <= 1e-3 of
+the kernel's bf16 output against the oracle's float64 result, on every
+named workload (sampled rows at full size) and on a sweep of shapes, edge
+cases and poisoned inputs."""
+
+import math
+import random
+
+import pytest
+import torch
+
+import oracle
+import paged_attention_kv_amd as pa
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+
+
+def banner(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def assert_close(got, want, what=""):
+    got = got.detach().cpu().double()
+    want = want.detach().cpu().double()
+    assert got.shape == want.shape
+    assert torch.isfinite(got).all(), f"{what}: non-finite output"
+    err = (got - want).abs()
+    mx, mean = err.max().item(), err.mean().item()
+    print(f"  {what}: max abs {mx:.3e} mean abs {mean:.3e} over {got.numel()} values", flush=True)
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max {mx:.3e} mean {mean:.3e}"
+
+
+def write_and_forward(case, hints=True, **kw):
+    pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
+    extra = {}
+    if hints:
+        extra = dict(max_query_len=max(case.spec.q_lens), max_seq_len=max(case.spec.seq_lens))
+    out = pa.forward(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                     case.query_start_loc, case.scale, **extra, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_rows(case, seqs, tokens_per_seq=None):
+    """Oracle output for the listed sequences (optionally only some of their
+    query rows), computed on a CPU copy of just the blocks they read.
+    Returns (flattened row indices, [R, Hq, D] float64)."""
+    q, kc, vc, table, lens, qsl, tmap = wl.sequences_subset(case, seqs)
+    pick = None
+    if tokens_per_seq is not None:
+        pick = []
+        for i, s in enumerate(seqs):
+            base = int(qsl[i])
+            pick.extend(base + r for r in tokens_per_seq[s])
+    want = oracle.ref_forward(q, kc, vc, table, lens, qsl, case.scale, tokens=pick)
+    rows = list(range(q.shape[0])) if pick is None else pick
+    return tmap[rows], want[rows]
+
+
+# ---------------------------------------------------------------------------
+# KV write
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_cache_write_bit_exact(i):
+    spec = wl.config(i)
+    banner(f"cache_write workload {i} ({spec.name}) T={spec.num_tokens}")
+    case = wl.make_case(spec, device=DEV)
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
+    torch.cuda.synchronize()
+    # oracle on a CPU copy of the touched blocks
+    slots = case.slot_mapping.cpu()
+    blocks = torch.unique(slots[slots >= 0] // 16)
+    remap = torch.full((spec.num_blocks,), -1, dtype=torch.int64)
+    remap[blocks] = torch.arange(blocks.numel())
+    local = torch.where(slots >= 0, remap[slots.clamp(min=0) // 16] * 16 + slots.clamp(min=0) % 16,
+                        slots)
+    kc_ref = k0[blocks.to(DEV)].cpu()
+    vc_ref = v0[blocks.to(DEV)].cpu()
+    oracle.ref_cache_write(case.k.cpu(), case.v.cpu(), local, kc_ref, vc_ref)
+    assert torch.equal(case.k_cache[blocks.to(DEV)].cpu().view(torch.int16), kc_ref.view(torch.int16))
+    assert torch.equal(case.v_cache[blocks.to(DEV)].cpu().view(torch.int16), vc_ref.view(torch.int16))
+    # every other block is untouched
+    keep = torch.ones(spec.num_blocks, dtype=torch.bool, device=DEV)
+    keep[blocks.to(DEV)] = False
+    assert torch.equal(case.k_cache[keep].view(torch.int16), k0[keep].view(torch.int16))
+    assert torch.equal(case.v_cache[keep].view(torch.int16), v0[keep].view(torch.int16))
+
+
+def test_cache_write_skips_negative_slots():
+    spec = wl.custom("pad", 8, 2, 64, rows=[(5, 3), (2, 20)], seed=3)
+    case = wl.make_case(spec, device=DEV)
+    slots = case.slot_mapping.clone()
+    slots[1] = -1
+    slots[4] = -7
+    k0 = case.k_cache.clone()
+    pa.cache_write(case.k, case.v, slots, case.k_cache, case.v_cache)
+    torch.cuda.synchronize()
+    ref = k0.cpu()
+    oracle.ref_cache_write(case.k.cpu(), case.v.cpu(), slots.cpu(), ref, ref.clone())
+    assert torch.equal(case.k_cache.cpu().view(torch.int16), ref.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Attention on the named workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hints", [True, False])
+def test_tiny_prefill_all_rows(hints):
+    spec = wl.config(1)
+    banner(f"forward workload 1 (tiny) hints={hints}")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case, hints=hints)
+    rows, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[rows], want, "tiny")
+
+
+def test_decode_workload_all_rows():
+    spec = wl.config(2)
+    banner("forward workload 2 (decode, 64 rows)")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case)
+    rows, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[rows], want, "decode")
+
+
+def test_mixed_workload_sampled_rows():
+    spec = wl.config(3)
+    banner("forward workload 3 (mixed 8192-token step), sampled rows")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case).cpu()
+    lens = spec.seq_lens
+    dec = sorted(range(256), key=lambda s: lens[s])
+    dec_pick = sorted(set(dec[:4] + dec[-4:] + random.Random(3).sample(range(256), 12)))
+    rows, want = oracle_rows(case, dec_pick)
+    assert_close(out[rows], want, "mixed/decode rows")
+    edge = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 127, 128, 1023, 1024, 1982, 1983]
+    per = {s: sorted(set(edge + random.Random(s).sample(range(1984), 16))) for s in range(256, 260)}
+    rows, want = oracle_rows(case, list(range(256, 260)), per)
+    assert_close(out[rows], want, "mixed/prefill rows")
+
+
+def test_long_decode_sampled_rows():
+    spec = wl.config(4)
+    banner("forward workload 4 (16 x 32768 decode), 3 rows")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case).cpu()
+    rows, want = oracle_rows(case, [0, 7, 15])
+    assert_close(out[rows], want, "long decode")
+
+
+def test_prefix_shared_sampled_rows():
+    spec = wl.config(5)
+    banner("forward workload 5 (prefix-shared decode), 16 rows")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case).cpu()
+    pick = sorted(random.Random(5).sample(range(256), 14) + [0, 255])
+    rows, want = oracle_rows(case, pick)
+    assert_close(out[rows], want, "prefix shared")
+
+
+# ---------------------------------------------------------------------------
+# Sweep of shapes and edge cases (small enough for the full oracle)
+# ---------------------------------------------------------------------------
+
+SWEEP_HEADS = [(8, 8), (16, 8), (32, 8), (32, 4), (64, 4), (16, 1)]
+EDGE_CTX = [0, 1, 14, 15, 16, 17, 31, 32, 33, 100, 300]
+EDGE_QL = [0, 1, 1, 2, 5, 16, 17, 33, 130]
+
+
+def sweep_rows(seed, n):
+    r = random.Random(seed)
+    rows = []
+    for _ in range(n):
+        ql = r.choice(EDGE_QL)
+        c = r.choice(EDGE_CTX)
+        if ql == 0 and c == 0:
+            c = 1
+        rows.append((ql, c))
+    return rows
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", SWEEP_HEADS)
+def test_sweep_full_oracle(d, hq, hkv):
+    rows = sweep_rows(hash((d, hq, hkv)) % 1000, 10)
+    spec = wl.custom(f"sweep_d{d}_{hq}x{hkv}", hq, hkv, d, rows=rows, seed=100 + hq + d)
+    banner(f"sweep D={d} Hq={hq} Hkv={hkv} rows={rows}")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case, hints=(d == 128))
+    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
+    r, want = oracle_rows(case, seqs)
+    assert_close(out.cpu()[r], want, spec.name)
+
+
+@pytest.mark.parametrize("part", [None])
+def test_long_context_split_into_many_partitions(part):
+    rows = [(1, 5000), (1, 17), (1, 2048), (1, 2049), (3, 4000), (1, 1023)]
+    spec = wl.custom("longsplit", 32, 4, 64, rows=rows, seed=41)
+    banner(f"long rows {rows}")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case, hints=False)
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "longsplit")
+
+
+def test_nan_poison_outside_context_does_not_leak():
+    rows = [(1, 18), (7, 9), (1, 31), (40, 0), (1, 1)]
+    spec = wl.custom("nanpoison", 32, 8, 128, rows=rows, seed=42)
+    banner("NaN-poisoned pool")
+    case = wl.make_case(spec, device=DEV, poison=float("nan"))
+    out = write_and_forward(case)
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "nan poison")
+
+
+def test_table_padding_poisoned_with_int32_max():
+    rows = [(1, 40), (9, 30), (1, 3)]
+    spec = wl.custom("padmax", 16, 2, 64, rows=rows, seed=43, max_blocks_per_seq=40)
+    case = wl.make_case(spec, device=DEV, table_pad=2**31 - 1)
+    banner("table padding = INT32_MAX")
+    out = write_and_forward(case, hints=False)
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "int32max padding")
+
+
+def test_row_order_does_not_matter_and_runs_are_deterministic():
+    rows = [(1, 700), (33, 100), (1, 64), (2, 2), (1, 3000), (20, 0)]
+    spec = wl.custom("order", 32, 8, 128, rows=rows, seed=44)
+    rev = wl.custom("order_rev", 32, 8, 128, rows=rows[::-1], seed=44)
+    banner("row order + determinism")
+    a = wl.make_case(spec, device=DEV)
+    out1 = write_and_forward(a).clone()
+    out2 = pa.forward(a.q, a.k_cache, a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
+                      a.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    b = wl.make_case(rev, device=DEV)
+    outb = write_and_forward(b)
+    r, want = oracle_rows(b, list(range(rev.num_seqs)))
+    assert_close(outb.cpu()[r], want, "reversed rows")
+
+
+def test_chunked_prefill_matches_one_shot():
+    """The pages' x-y-z example on the GPU: an 18-token prompt (after 40
+    cached tokens) run as chunks of 8, 8 and 2 with a cache write before each
+    step, against one 18-token step; both against the oracle."""
+    Hq, Hkv, D, c, P = 32, 8, 128, 40, 18
+    spec = wl.custom("oneshot", Hq, Hkv, D, rows=[(P, c)], seed=45, num_blocks=64)
+    case = wl.make_case(spec, device=DEV)
+    banner("chunked prefill 8+8+2 vs one shot")
+    kc0, vc0 = case.k_cache.clone(), case.v_cache.clone()
+    one = write_and_forward(case)
+    r, want = oracle_rows(case, [0])
+    assert_close(one.cpu()[r], want, "one shot")
+    kc, vc = kc0, vc0
+    outs = []
+    lo = 0
+    for n in oracle.chunk_plan(P, 8):
+        sl = slice(lo, lo + n)
+        pa.cache_write(case.k[sl].contiguous(), case.v[sl].contiguous(),
+                       case.slot_mapping[sl].contiguous(), kc, vc)
+        o = pa.forward(case.q[sl].contiguous(), kc, vc, case.block_table,
+                       torch.tensor([c + lo + n], dtype=torch.int32, device=DEV),
+                       torch.tensor([0, n], dtype=torch.int32, device=DEV), case.scale)
+        outs.append(o)
+        lo += n
+    torch.cuda.synchronize()
+    assert len(outs) == 3
+    chunked = torch.cat(outs)
+    assert_close(chunked.cpu(), want, "chunked")
+    assert (chunked.double() - one.double()).abs().max().item() <= MAX_ABS
+
+
+def test_validate_inputs_accepts_good_and_names_bad_metadata():
+    spec = wl.custom("val", 8, 2, 64, rows=[(1, 20), (4, 4)], seed=46)
+    case = wl.make_case(spec, device=DEV)
+    pa.validate_inputs(case.block_table, case.seq_lens, case.query_start_loc, spec.num_tokens,
+                       spec.num_blocks, slot_mapping=case.slot_mapping)
+    bad = case.seq_lens.clone()
+    bad[1] = 2   # fewer tokens than query rows
+    with pytest.raises(pa.PaError, match="seq_len"):
+        pa.validate_inputs(case.block_table, bad, case.query_start_loc, spec.num_tokens,
+                           spec.num_blocks)
+    dup = case.slot_mapping.clone()
+    dup[1] = dup[0]
+    with pytest.raises(pa.PaError, match="twice"):
+        pa.validate_inputs(case.block_table, case.seq_lens, case.query_start_loc,
+                           spec.num_tokens, spec.num_blocks, slot_mapping=dup)
+    tbl = case.block_table.clone()
+    tbl[0, 0] = spec.num_blocks
+    with pytest.raises(pa.PaError, match="block_table"):
+        pa.validate_inputs(tbl, case.seq_lens, case.query_start_loc, spec.num_tokens,
+                           spec.num_blocks)
