@@ -43,6 +43,7 @@ METRIC = "paged-attn decode GB/s (% of 8 TB/s) + mixed-step tokens/s on 1 MI355X
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATIONS = 8
+COPY_MIB = 512
 
 
 # ---------------------------------------------------------------------------
@@ -97,7 +98,8 @@ class StepInputs:
             for b0 in range(0, NB, chunk):
                 b1 = min(NB, b0 + chunk)
                 cache[b0:b1] = torch.randn((b1 - b0, bs, Hkv, D), generator=gen, device=device)
-        nb_per_set = sum(-(-L // bs) for L in spec.seq_lens)
+        P = spec.shared_prefix_blocks
+        nb_per_set = P + sum(-(-L // bs) - P for L in spec.seq_lens)
         if rotations * nb_per_set > NB:
             rotations = max(1, NB // nb_per_set)
         self.rotations = rotations
@@ -107,10 +109,13 @@ class StepInputs:
         for r in range(rotations):
             table = torch.full((S, MB), -1, dtype=torch.int32)
             slots = []
+            shared = perm[used:used + P].to(torch.int32)
+            used += P
             for s, (ql, L) in enumerate(zip(spec.q_lens, spec.seq_lens)):
                 nb = -(-L // bs)
-                table[s, :nb] = perm[used:used + nb].to(torch.int32)
-                used += nb
+                table[s, :P] = shared
+                table[s, P:nb] = perm[used:used + nb - P].to(torch.int32)
+                used += nb - P
                 pos = torch.arange(L - ql, L)
                 slots.append(table[s, pos // bs].to(torch.int64) * bs + pos % bs)
             self.sets.append(dict(
@@ -128,39 +133,44 @@ class StepInputs:
         self.hints = dict(max_query_len=max(spec.q_lens), max_seq_len=max(spec.seq_lens))
 
 
-def run_steps(pa, inp: StepInputs, steps: int, warmup: int, rows=None):
-    """Time `steps` steps (write + forward); also HIP-event time of each
-    pa_forward call on the launch stream. Returns (ms/step, ms/forward)."""
-    spec = inp.spec
-    if rows is not None:
-        raise ValueError("sub-batch timing uses its own StepInputs")
+FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan")
 
-    def step(i, ev=None):
+
+def run_steps(pa, inp: StepInputs, steps: int, warmup: int):
+    """Time `steps` steps (KV write + forward). Pass 1 is bracketed by
+    synchronize and timed with HIP events on the launch stream, with nothing
+    else inside (the step time). Pass 2 repeats the steps with the library's
+    kernel timing on (pa.profile_begin/end: HIP events around every kernel
+    launch on its stream). Returns (ms per step, {kernel class: mean ms per
+    launch}, {kernel class: launches per step}, ms of forward kernels per
+    step)."""
+    spec = inp.spec
+
+    def step(i):
         st = inp.sets[i % inp.rotations]
         pa.cache_write(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache)
-        if ev is not None:
-            ev[0].record()
         pa.forward(st["q"], inp.k_cache, inp.v_cache, st["block_table"], inp.seq_lens, inp.qsl,
                    spec.scale, out=st["out"], **inp.hints)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for i in range(steps):
-        step(i, evs[i])
+        step(i)
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
-    fwd = sorted(a.elapsed_time(b) for a, b in evs)
-    return ms_step, sum(fwd) / len(fwd), fwd[len(fwd) // 2]
+    pa.profile_begin()
+    for i in range(steps):
+        step(i)
+    per = pa.profile_end()
+    mean = {k: v[1] / v[0] for k, v in per.items()}
+    count = {k: v[0] / steps for k, v in per.items()}
+    ms_fwd = sum(per[k][1] for k in FORWARD_KERNELS if k in per) / steps
+    return ms_step, mean, count, ms_fwd
 
 
 def sub_spec(spec, rows, name):
@@ -211,7 +221,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mixed"], default=None)
+    ap.add_argument("--only", choices=["decode", "mixed", "long", "prefix", "tiny", "copy"],
+                    default=None)
+    ap.add_argument("--all", action="store_true",
+                    help="also time the long-decode, prefix-shared and tiny workloads")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -224,25 +237,37 @@ def main(argv=None):
     pa.load_library()
     dev = "cuda:0"
     result = {}
+    if args.only == "copy":
+        # Calibration for the HBM byte counters: a plain device-to-device copy
+        # of a known size (COPY_MIB read + COPY_MIB written per launch).
+        n = COPY_MIB << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": COPY_MIB, "launches": args.warmup + args.steps}), flush=True)
+        return 0
 
     if args.only in (None, "decode"):
         spec = wl.config(2)
         inp = StepInputs(spec, ROTATIONS, dev)
-        ms_step, ms_fwd, ms_fwd_med = run_steps(pa, inp, args.steps, args.warmup)
+        ms_step, kmean, kcount, ms_fwd = run_steps(pa, inp, args.steps, args.warmup)
         b_attn = attention_bytes(spec)
         b_step = b_attn + write_bytes(spec)
         gbs = b_step / (ms_step * 1e-3) / 1e9
-        kern_gbs = b_attn / (ms_fwd * 1e-3) / 1e9
-        result["decode"] = dict(ms_step=ms_step, gbs=gbs, ms_fwd=ms_fwd, ms_fwd_median=ms_fwd_med,
-                                fwd_gbs=kern_gbs, bytes_step=b_step, bytes_fwd=b_attn,
-                                rotations=inp.rotations)
+        ms_dec = kmean["decode"]
+        result["decode"] = dict(ms_step=ms_step, gbs=gbs, ms_fwd=ms_fwd, ms_decode_kernel=ms_dec,
+                                kernel_gbs=b_attn / (ms_dec * 1e-3) / 1e9, bytes_step=b_step,
+                                bytes_fwd=b_attn, rotations=inp.rotations,
+                                kernels={k: round(v * 1e3, 3) for k, v in kmean.items()})
         del inp
         torch.cuda.empty_cache()
 
     if args.only in (None, "mixed"):
         spec = wl.config(3)
         inp = StepInputs(spec, 1, dev)
-        ms_step, ms_fwd, ms_fwd_med = run_steps(pa, inp, max(5, args.steps // 5),
+        ms_step, kmean_m, _, ms_fwd = run_steps(pa, inp, max(5, args.steps // 5),
                                                 max(2, args.warmup // 2))
         dec_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] == 1]
         pre_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 1]
@@ -252,12 +277,39 @@ def main(argv=None):
         for name, rows in (("decode_rows", dec_rows), ("prefill_rows", pre_rows)):
             ss = sub_spec(spec, rows, name)
             si = StepInputs(ss, 1, dev)
-            _, f_ms, _ = run_steps(pa, si, max(5, args.steps // 5), 2)
-            sub[name] = dict(ms_fwd=f_ms, bytes=attention_bytes(ss), flops=attention_flops(ss))
+            _, km, _, f_ms = run_steps(pa, si, max(5, args.steps // 5), 2)
+            sub[name] = dict(ms_fwd=f_ms, bytes=attention_bytes(ss), flops=attention_flops(ss),
+                             kernels={k: round(v * 1e3, 3) for k, v in km.items()})
             del si
             torch.cuda.empty_cache()
         tok_s = spec.num_tokens / (ms_step * 1e-3)
-        result["mixed"] = dict(ms_step=ms_step, tokens_per_s=tok_s, ms_fwd=ms_fwd, sub=sub)
+        result["mixed"] = dict(ms_step=ms_step, tokens_per_s=tok_s, ms_fwd=ms_fwd, sub=sub,
+                               kernels={k: round(v * 1e3, 3) for k, v in kmean_m.items()})
+
+    others = []
+    if args.all or args.only in ("long", "prefix", "tiny"):
+        for name, i, rot in (("long", 4, 1), ("prefix", 5, ROTATIONS), ("tiny", 1, 1)):
+            if args.only not in (None, name):
+                continue
+            spec = wl.config(i)
+            inp = StepInputs(spec, rot, dev)
+            ms_step, km, _, ms_fwd = run_steps(pa, inp, args.steps, args.warmup)
+            b = attention_bytes(spec)
+            entry = dict(workload=spec.description, ms_per_step=round(ms_step, 5),
+                         ms_forward_kernels=round(ms_fwd, 5), rotations=inp.rotations,
+                         forward_gbs_logical=round(b / (ms_fwd * 1e-3) / 1e9, 2),
+                         kernel_avg_us={k: round(v * 1e3, 3) for k, v in km.items()},
+                         tokens_per_s=round(spec.num_tokens / (ms_step * 1e-3), 1))
+            if i == 5:
+                uniq = (spec.shared_prefix_blocks + spec.num_seqs * (
+                    spec.max_blocks_per_seq - spec.shared_prefix_blocks)) * \
+                    2 * spec.block_size * spec.num_kv_heads * spec.head_size * 2
+                entry["forward_gbs_unique"] = round(uniq / (ms_fwd * 1e-3) / 1e9, 2)
+            if i == 4:
+                entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            others.append((name, entry))
+            del inp
+            torch.cuda.empty_cache()
 
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -272,13 +324,14 @@ def main(argv=None):
             "tokens": 64, "kv_bytes_per_step": d["bytes_step"],
             "block_table_rotations": d["rotations"],
             "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
-        line["roofline"] = {"bound": "hbm", "kernel": "pa_forward (decode_partition_kernel)",
-                            "achieved": round(d["fwd_gbs"], 2), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(d["fwd_gbs"] / HBM_PEAK_GBS, 4),
+        line["roofline"] = {"bound": "hbm", "kernel": "decode_partition_kernel<64,3>",
+                            "achieved": round(d["kernel_gbs"], 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
                             "traffic": None,
-                            "avg_launch_us": round(d["ms_fwd"] * 1e3, 3),
-                            "median_launch_us": round(d["ms_fwd_median"] * 1e3, 3),
-                            "algorithmic_bytes_per_launch": d["bytes_fwd"]}
+                            "avg_launch_us": round(d["ms_decode_kernel"] * 1e3, 3),
+                            "algorithmic_bytes_per_launch": d["bytes_fwd"],
+                            "forward_kernels_us_per_step": round(d["ms_fwd"] * 1e3, 3),
+                            "kernel_avg_us": d["kernels"]}
     if "mixed" in result:
         m = result["mixed"]
         pre = m["sub"]["prefill_rows"]
@@ -288,12 +341,15 @@ def main(argv=None):
                          "U[256,8192]) + 4 chunks of 1984 tokens (prior context U[0,4096]); "
                          "32 q / 8 kv heads, head_size 128"),
             "tokens_per_s": round(m["tokens_per_s"], 1), "unit": "tokens/s",
-            "ms_per_step": round(m["ms_step"], 4), "ms_forward": round(m["ms_fwd"], 4),
+            "ms_per_step": round(m["ms_step"], 4), "ms_forward_kernels": round(m["ms_fwd"], 4),
+            "kernel_avg_us": m["kernels"],
             "prefill_rows": {"ms": round(pre["ms_fwd"], 4), "flops": pre["flops"],
+                             "kernel_avg_us": pre["kernels"],
                              "tflops": round(pre["flops"] / (pre["ms_fwd"] * 1e-3) / 1e12, 2),
                              "frac_of_bf16_peak": round(pre["flops"] / (pre["ms_fwd"] * 1e-3)
                                                         / 1e12 / BF16_PEAK_TFLOPS, 4)},
             "decode_rows": {"ms": round(dec["ms_fwd"], 4), "bytes": dec["bytes"],
+                            "kernel_avg_us": dec["kernels"],
                             "gbs": round(dec["bytes"] / (dec["ms_fwd"] * 1e-3) / 1e9, 2),
                             "frac_of_hbm_peak": round(dec["bytes"] / (dec["ms_fwd"] * 1e-3)
                                                       / 1e9 / HBM_PEAK_GBS, 4)}}
@@ -301,6 +357,12 @@ def main(argv=None):
             line.update(value=round(m["tokens_per_s"], 1), unit="tokens/s",
                         ms_per_step=round(m["ms_step"], 5),
                         config={"workload": line["mixed_step"]["workload"]})
+    for name, entry in others:
+        line.setdefault("other_workloads", {})[name] = entry
+    if "value" not in line and others:
+        name, entry = others[0]
+        line.update(value=entry["forward_gbs_logical"], unit="GB/s",
+                    ms_per_step=entry["ms_per_step"], config={"workload": entry["workload"]})
     if not args.no_cpu and "decode" in result:
         line["cpu_baseline"] = cpu_baseline(wl.config(2))
     print(json.dumps(line), flush=True)

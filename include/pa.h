@@ -86,9 +86,11 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    int64_t num_blocks, int32_t block_size, void* stream);
 
 /*
- * Workspace bytes pa_forward needs for these sizes (the split-K partial
- * results of decode rows and the work list of prefill tiles). Depends only
- * on its arguments; returns 0 if an argument is out of range.
+ * Workspace bytes pa_forward needs for these sizes: a fixed 256 KiB region
+ * of split-K arrival counters at the start (never written with anything
+ * else, so one zero-filled workspace can serve calls of any shape), then the
+ * split-K partial results of decode rows and the work list of prefill tiles.
+ * Depends only on its arguments; returns 0 if an argument is out of range.
  * max_seq_len_hint <= 0 means "unknown" (max_blocks_per_seq * 16 is used).
  */
 size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
@@ -114,10 +116,11 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  *                    <= 0 = unknown (num_tokens and max_blocks_per_seq * 16
  *                    are used). A hint below the true maximum is a contract
  *                    violation (rows past it are not computed).
- *   workspace        device, >= pa_forward_workspace_bytes(...) bytes, 256-
- *                    byte aligned; contents need no initialisation and are
- *                    scratch after the call. Calls that share a workspace
- *                    must be ordered on one stream.
+ *   workspace        device, >= pa_forward_workspace_bytes(...) bytes,
+ *                    16-byte aligned, zero-filled before its first use: it
+ *                    holds split-K arrival counters that every call leaves at
+ *                    zero again, the rest is scratch. Calls that share a
+ *                    workspace must be ordered on one stream.
  *
  * Query row i of sequence s (i < q_len = qsl[s+1] - qsl[s]) sits at position
  * c + i with c = seq_lens[s] - q_len and attends to keys 0..c+i of its own
@@ -125,6 +128,11 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * Rows with q_len == 0 produce nothing; rows with q_len == 1 take the decode
  * path (split-K over the context), rows with q_len > 1 the prefill path.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
+ * Tuning overrides, read once per process (for sweeps; out-of-range values
+ * are ignored): PA_DECODE_PART_TOKENS (split-K partition, 128..1024, a
+ * multiple of 16), PA_DECODE_PREFETCH (blocks in flight per wave, 2..4),
+ * PA_DECODE_FUSED_MAX (rows with at most this many partitions are merged by
+ * their last workgroup, 0..16; 0 = always use the combine kernel).
  * Requires block_size == 16, head_size in {64, 128}, num_q_heads /
  * num_kv_heads in {1, 2, 4, 8, 16}. Caller contract: 0 <= q_len <= seq_len
  * <= max_blocks_per_seq * 16 and the first ceil(seq_len / 16) table entries
@@ -153,6 +161,32 @@ int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
                        int32_t num_tokens, int32_t num_seqs, int32_t max_blocks_per_seq,
                        int64_t num_blocks, int32_t block_size, int32_t num_write_tokens,
                        int32_t max_query_len_hint, int32_t max_seq_len_hint, void* stream);
+
+/*
+ * Kernel timing for measurement harnesses (not for the hot path). After
+ * pa_profile_begin, every kernel the library launches is bracketed by HIP
+ * events on its stream; pa_profile_end stops recording, waits for those
+ * events and returns, per kernel class, the number of launches and their
+ * summed elapsed time (event to event, on the launch stream). Begin resets
+ * the totals. Recording is process-wide and off by default; while it is off
+ * a launch pays one atomic flag read. Events are created on first use and
+ * reused.
+ */
+#define PA_KERNEL_CACHE_WRITE 0   /* pa_cache_write                            */
+#define PA_KERNEL_DECODE 1        /* decode rows: partitions                   */
+#define PA_KERNEL_COMBINE 2       /* decode rows: split-K merge                */
+#define PA_KERNEL_PREFILL 3       /* prefill tiles seeing many keys            */
+#define PA_KERNEL_PREFILL_SHORT 4 /* prefill tiles seeing few keys             */
+#define PA_KERNEL_PLAN 5          /* prefill tile planner                      */
+#define PA_KERNEL_CLASSES 8
+
+typedef struct pa_profile {
+  int64_t launches[PA_KERNEL_CLASSES];
+  double total_ms[PA_KERNEL_CLASSES];
+} pa_profile;
+
+int pa_profile_begin(void);
+int pa_profile_end(pa_profile* out);  /* out may be NULL */
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* pa_last_error(void);

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["cache_write", "forward", "forward_workspace_bytes", "validate_inputs",
            "kv_block_bytes", "last_error", "version", "library_path", "load_library",
-           "PaError", "BLOCK_SIZE"]
+           "profile_begin", "profile_end", "PaError", "BLOCK_SIZE", "KERNEL_CLASSES"]
 
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,9 +43,21 @@ SIGNATURES = {
                                   _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
     "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                           _I32, _I32, _P]),
+    "pa_profile_begin": (ctypes.c_int, []),
+    "pa_profile_end": (ctypes.c_int, [_P]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_version": (ctypes.c_char_p, []),
 }
+
+
+# Kernel classes of the timing facility (PA_KERNEL_* in include/pa.h).
+KERNEL_CLASSES = {0: "cache_write", 1: "decode", 2: "combine", 3: "prefill",
+                  4: "prefill_short", 5: "plan"}
+_NCLASS = 8
+
+
+class _Profile(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64 * _NCLASS), ("total_ms", ctypes.c_double * _NCLASS)]
 
 
 class PaError(RuntimeError):
@@ -146,7 +158,9 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        # zero-filled once: the split-K arrival counters must start at zero
+        # (the library leaves them zero after every call)
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -159,8 +173,8 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
     paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
     ``max_seq_len`` are optional host upper bounds that shrink the launch
-    grids; ``workspace`` (uint8, on the device) is taken from a per-device
-    cache when omitted."""
+    grids; ``workspace`` (uint8, on the device, zero-filled before its first
+    use) is taken from a per-device cache when omitted."""
     lib = load_library()
     _dev_tensor("q", q, torch.bfloat16, 3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -211,3 +225,18 @@ def validate_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor,
                                   num_tokens, S, MB, num_blocks, BLOCK_SIZE, nw,
                                   max_query_len or 0, max_seq_len or 0,
                                   _stream(block_table)))
+
+
+def profile_begin() -> None:
+    """Start timing every kernel launch of the library with HIP events on its
+    stream (measurement harnesses only; see pa_profile_begin)."""
+    _check(load_library().pa_profile_begin())
+
+
+def profile_end() -> dict:
+    """Stop timing; wait for the recorded events and return
+    {class name: (launches, total ms)} for every class that launched."""
+    prof = _Profile()
+    _check(load_library().pa_profile_end(ctypes.byref(prof)))
+    return {KERNEL_CLASSES.get(c, str(c)): (int(prof.launches[c]), float(prof.total_ms[c]))
+            for c in range(_NCLASS) if prof.launches[c]}

@@ -36,9 +36,11 @@ hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slot_
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
+  profile_begin(PA_KERNEL_CACHE_WRITE, stream);
   hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
                      (u32x4*)v_cache, total, chunks_per_token);
+  profile_end(PA_KERNEL_CACHE_WRITE, stream);
   return hipGetLastError();
 }
 

@@ -62,17 +62,45 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
       (__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// Cross-lane reductions over lanes that differ in bit 4 and bit 5 of the lane
-// id, i.e. across the four 16-lane groups of a wave.
+// Values of lane l and lane l ^ 16 (v_permlane16_swap) or l ^ 32
+// (v_permlane32_swap): both results of the swap, in either order.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Reductions across the four 16-lane groups of a wave (lanes that differ in
+// bits 4 and 5 of the lane id), on the VALU.
 __device__ __forceinline__ float max_across_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a, b;
+  pair16(v, a, b);
+  v = fmaxf(a, b);
+  pair32(v, a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float sum_across_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a, b;
+  pair16(v, a, b);
+  v = a + b;
+  pair32(v, a, b);
+  return a + b;
+}
+
+// Device-coherent 32-bit store and load (agent scope, relaxed): the store
+// writes through this XCD's L2 and the load does not hit a stale line in it,
+// so workgroups on different XCDs can hand data over without flushing or
+// invalidating whole caches.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Orders this wave's LDS writes before its later LDS reads (and the reverse)

@@ -6,7 +6,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
+
+// Brackets one kernel launch of class `cls` (PA_KERNEL_*) with timing events
+// when pa_profile_begin has enabled recording; otherwise no-ops.
+void profile_begin(int cls, hipStream_t stream);
+void profile_end(int cls, hipStream_t stream);
 
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                               void* k_cache, void* v_cache, int32_t num_tokens,
@@ -28,26 +35,36 @@ struct ForwardArgs {
 // Decode rows (q_len == 1): split-K partials or direct output, then combine.
 struct DecodePlan {
   int32_t part_tokens;    // tokens per split-K partition (multiple of 16)
-  int32_t num_parts_max;  // partitions reserved per row in the workspace
+  int32_t num_parts_max;  // partitions per row (grid x; workspace stride)
+  int32_t prefetch;       // register ring depth in 16-token blocks (2..4)
+  bool fused;             // last-arriving workgroup merges (else a combine kernel)
   float* ws_o;            // [S][num_parts_max][Hq][D] unnormalised partial outputs
-  float* ws_ml;           // [S][num_parts_max][Hq][2] running max (log2 units) and sum
+  float* ws_ml;           // [S][num_parts_max][Hq][2] reference max (log2 units) and sum
+  int32_t* counters;      // [S][decode_groups(Hkv)] arrival counters, zero between calls
 };
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream);
+// Workgroups along the KV-head axis of the decode grid.
+int32_t decode_groups(int32_t num_kv_heads);
 
 // Prefill rows (q_len > 1): a planner writes the tile list, then the tiles run.
 struct PrefillPlan {
   int32_t tile_queries;  // query tokens per tile
-  int32_t tile_bound;    // entries in the tile list (upper bound on tiles)
-  int32_t* tiles;        // [tile_bound] (sequence << 16 | tile index) or -1
+  int32_t bound_a;       // entries of list A (tiles seeing many keys)
+  int32_t bound_b;       // entries of list B (tiles seeing few keys)
+  int32_t* tiles_a;      // [bound_a][2] (sequence, first query row) or -1
+  int32_t* tiles_b;      // [bound_b][2]
+  int32_t* counts;       // [2] tiles the planner put in lists A and B
 };
 hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
 // Query tokens per prefill tile for a given group size (128 MFMA rows / G).
 int32_t prefill_tile_queries(int32_t group);
+// Upper bound on list-B tiles per row.
+int32_t prefill_split_tiles_per_row(int32_t group);
 
 // Workspace layout shared by pa_forward and pa_forward_workspace_bytes.
 struct WorkspaceLayout {
-  int32_t part_tokens, num_parts_max, tile_queries, tile_bound;
-  size_t off_o, off_ml, off_tiles, total;
+  int32_t part_tokens, num_parts_max, tile_queries, bound_a, bound_b;
+  size_t off_ctr, off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
 };
 bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,

@@ -37,8 +37,19 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 constexpr int32_t kMinPartTokens = 128;
 constexpr int32_t kMaxPartTokens = 1024;
 constexpr size_t kAlign = 256;
+// Split-K arrival counters sit in a region of fixed size at the start of
+// every workspace, so no call of any shape ever writes data over the
+// counters another call relies on being zero.
+constexpr int64_t kCounterSlots = 1 << 16;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int env_int(const char* name, int lo, int hi, int dflt) {
+  const char* e = getenv(name);
+  if (!e) return dflt;
+  const int v = atoi(e);
+  return (v >= lo && v <= hi) ? v : dflt;
+}
 
 int32_t resolved_max_seq_len(int32_t max_blocks_per_seq, int32_t hint) {
   const int32_t cap = max_blocks_per_seq * PA_BLOCK_SIZE;
@@ -51,10 +62,8 @@ int32_t resolved_max_seq_len(int32_t max_blocks_per_seq, int32_t hint) {
 // [128, 1024]) for tuning sweeps.
 int32_t choose_part_tokens(int32_t num_seqs, int32_t max_len) {
   static const int32_t env = [] {
-    const char* e = getenv("PA_DECODE_PART_TOKENS");
-    if (!e) return 0;
-    const int v = atoi(e);
-    return (v >= kMinPartTokens && v <= kMaxPartTokens && v % PA_BLOCK_SIZE == 0) ? v : 0;
+    const int v = env_int("PA_DECODE_PART_TOKENS", kMinPartTokens, kMaxPartTokens, 0);
+    return v % PA_BLOCK_SIZE == 0 ? v : 0;
   }();
   if (env) return env;
   for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
@@ -65,6 +74,22 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t max_len) {
 }
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Register ring depth of the decode kernel (blocks in flight per wave);
+// PA_DECODE_PREFETCH overrides it for tuning sweeps.
+int32_t decode_prefetch() {
+  static const int v = env_int("PA_DECODE_PREFETCH", 2, 4, 3);
+  return v;
+}
+
+// Rows with at most this many partitions are merged by their last-arriving
+// workgroup, the others by the separate combine kernel. PA_DECODE_FUSED_MAX
+// sets it (0..16); the default 0 always uses the combine kernel, which
+// measured faster on every workload tried.
+int32_t fused_max_parts() {
+  static const int v = env_int("PA_DECODE_FUSED_MAX", 0, 16, 0);
+  return v;
+}
 
 }  // namespace
 
@@ -84,12 +109,19 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   // Reserve for the smallest partition size so any tuning choice fits.
   w.num_parts_max = (max_len + kMinPartTokens - 1) / kMinPartTokens;
   w.tile_queries = prefill_tile_queries(group);
-  w.tile_bound = (num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
+  // Each row adds at most one partial tile: sum ceil(ql/BQ) <= T/BQ + S.
+  const int64_t any_bound = (int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
+  w.bound_a = (int32_t)any_bound;
+  w.bound_b = (int32_t)std::min<int64_t>(
+      any_bound, (int64_t)num_seqs * prefill_split_tiles_per_row(group));
   const size_t rows = (size_t)num_seqs * w.num_parts_max * num_q_heads;
-  w.off_o = 0;
+  w.off_ctr = 0;
+  w.off_o = round_up((size_t)kCounterSlots * sizeof(int32_t), kAlign);
   w.off_ml = round_up(w.off_o + rows * head_size * sizeof(float), kAlign);
-  w.off_tiles = round_up(w.off_ml + rows * 2 * sizeof(float), kAlign);
-  w.total = round_up(w.off_tiles + (size_t)w.tile_bound * 2 * sizeof(int32_t), kAlign);
+  w.off_counts = round_up(w.off_ml + rows * 2 * sizeof(float), kAlign);
+  w.off_tiles_a = w.off_counts + kAlign;
+  w.off_tiles_b = round_up(w.off_tiles_a + (size_t)w.bound_a * 2 * sizeof(int32_t), kAlign);
+  w.total = round_up(w.off_tiles_b + (size_t)w.bound_b * 2 * sizeof(int32_t), kAlign);
   *out = w;
   return true;
 }
@@ -211,16 +243,23 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
     pp.tile_queries = w.tile_queries;
     const int64_t by_hint =
         (int64_t)num_seqs * ((a.max_query_len + w.tile_queries - 1) / w.tile_queries);
-    pp.tile_bound = (int32_t)std::min<int64_t>(w.tile_bound, by_hint);
-    pp.tiles = (int32_t*)(ws + w.off_tiles);
+    pp.bound_a = (int32_t)std::min<int64_t>(w.bound_a, by_hint);
+    pp.bound_b = (int32_t)std::min<int64_t>(w.bound_b, by_hint);
+    pp.tiles_a = (int32_t*)(ws + w.off_tiles_a);
+    pp.tiles_b = (int32_t*)(ws + w.off_tiles_b);
+    pp.counts = (int32_t*)(ws + w.off_counts);
     hipError_t e = pa::launch_prefill(a, pp, st);
     if (e != hipSuccess) return hip_fail(e, "pa_forward prefill launch");
   }
   pa::DecodePlan dp;
   dp.part_tokens = w.part_tokens;
   dp.num_parts_max = (a.max_seq_len + w.part_tokens - 1) / w.part_tokens;
+  dp.prefetch = decode_prefetch();
+  dp.fused = dp.num_parts_max > 1 && dp.num_parts_max <= fused_max_parts() &&
+             (int64_t)num_seqs * pa::decode_groups(num_kv_heads) <= kCounterSlots;
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
+  dp.counters = (int32_t*)(ws + w.off_ctr);
   hipError_t e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward decode launch");
   return PA_OK;

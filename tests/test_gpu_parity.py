@@ -301,3 +301,19 @@ def test_validate_inputs_accepts_good_and_names_bad_metadata():
     with pytest.raises(pa.PaError, match="block_table"):
         pa.validate_inputs(tbl, case.seq_lens, case.query_start_loc, spec.num_tokens,
                            spec.num_blocks)
+
+
+def test_workspace_shared_by_calls_of_different_shapes():
+    """One cached workspace serves calls whose split-K layouts differ: a call
+    merged by its last workgroup, one merged by the combine kernel (many
+    partitions, fewer rows), then the first shape again. Regression test for
+    arrival counters that a later call's partials overwrote."""
+    fused = wl.custom("ws_fused", 32, 8, 128, rows=[(1, 4000)] * 40, seed=47)
+    many = wl.custom("ws_many", 64, 8, 128, rows=[(1, 30000), (1, 20000)], seed=48)
+    for spec in (fused, many, fused, many, fused):
+        banner(f"workspace reuse: {spec.name}")
+        case = wl.make_case(spec, device=DEV)
+        out = write_and_forward(case)
+        pick = list(range(0, spec.num_seqs, max(1, spec.num_seqs // 6)))
+        r, want = oracle_rows(case, pick)
+        assert_close(out.cpu()[r], want, spec.name)
