@@ -130,7 +130,8 @@ class StepInputs:
         for ql in spec.q_lens:
             qsl.append(qsl[-1] + ql)
         self.qsl = torch.tensor(qsl, dtype=torch.int32, device=device)
-        self.hints = dict(max_query_len=max(spec.q_lens), max_seq_len=max(spec.seq_lens))
+        self.hints = dict(max_query_len=max(spec.q_lens), max_seq_len=max(spec.seq_lens),
+                          shared_blocks=spec.shared_prefix_blocks > 0)
 
 
 FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan")
@@ -186,6 +187,35 @@ def sub_spec(spec, rows, name):
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 
+def decode_source_hash() -> str:
+    """Hash of the decode kernel's sources (decode.hip and common.h)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "common.h"):
+        with open(os.path.join(ROOT, "paged_attention_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size), or None when the summary is missing or was
+    taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_decode.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_src_sha256_16") != decode_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    if not k or "write_bytes" not in k:
+        return None
+    return int(k["read_bytes"] + k["write_bytes"])
+
+
 def cpu_baseline(spec, budget_s: float = 12.0):
     """Time the oracle (float64, as it stands) on all rows of the workload
     for about budget_s seconds of CPU work on this host."""
@@ -221,8 +251,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["decode", "mixed", "long", "prefix", "tiny", "copy"],
-                    default=None)
+    ap.add_argument("--only", choices=["decode", "mixed", "long", "prefix", "tiny", "copy",
+                                       "mixed_decode", "mixed_prefill"], default=None)
     ap.add_argument("--all", action="store_true",
                     help="also time the long-decode, prefix-shared and tiny workloads")
     args = ap.parse_args(argv)
@@ -287,15 +317,21 @@ def main(argv=None):
                                kernels={k: round(v * 1e3, 3) for k, v in kmean_m.items()})
 
     others = []
-    if args.all or args.only in ("long", "prefix", "tiny"):
-        for name, i, rot in (("long", 4, 1), ("prefix", 5, ROTATIONS), ("tiny", 1, 1)):
-            if args.only not in (None, name):
+    if args.all or args.only in ("long", "prefix", "tiny", "mixed_decode", "mixed_prefill"):
+        m3 = wl.config(3)
+        for name, i, rot in (("long", 4, 1), ("prefix", 5, ROTATIONS), ("tiny", 1, 1),
+                             ("mixed_decode", 3, 1), ("mixed_prefill", 3, 1)):
+            if args.only != name and (args.only is not None or name.startswith("mixed_")):
                 continue
             spec = wl.config(i)
+            if name == "mixed_decode":
+                spec = sub_spec(m3, [s for s in range(m3.num_seqs) if m3.q_lens[s] == 1], name)
+            if name == "mixed_prefill":
+                spec = sub_spec(m3, [s for s in range(m3.num_seqs) if m3.q_lens[s] > 1], name)
             inp = StepInputs(spec, rot, dev)
             ms_step, km, _, ms_fwd = run_steps(pa, inp, args.steps, args.warmup)
             b = attention_bytes(spec)
-            entry = dict(workload=spec.description, ms_per_step=round(ms_step, 5),
+            entry = dict(workload=spec.description or spec.name, ms_per_step=round(ms_step, 5),
                          ms_forward_kernels=round(ms_fwd, 5), rotations=inp.rotations,
                          forward_gbs_logical=round(b / (ms_fwd * 1e-3) / 1e9, 2),
                          kernel_avg_us={k: round(v * 1e3, 3) for k, v in km.items()},
@@ -324,10 +360,11 @@ def main(argv=None):
             "tokens": 64, "kv_bytes_per_step": d["bytes_step"],
             "block_table_rotations": d["rotations"],
             "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
-        line["roofline"] = {"bound": "hbm", "kernel": "decode_partition_kernel<64,3>",
+        line["roofline"] = {"bound": "hbm", "kernel": "decode_partition_kernel<64, 3, true>",
                             "achieved": round(d["kernel_gbs"], 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                            "traffic": None,
+                            "traffic": measured_traffic(
+                                "decode_partition_kernel<64, 3, true> @ decode (64 x U[512,2048], D 64)"),
                             "avg_launch_us": round(d["ms_decode_kernel"] * 1e3, 3),
                             "algorithmic_bytes_per_launch": d["bytes_fwd"],
                             "forward_kernels_us_per_step": round(d["ms_fwd"] * 1e3, 3),

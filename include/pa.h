@@ -147,6 +147,28 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
                size_t workspace_bytes, void* stream);
 
 /*
+ * pa_forward with option flags (pa_forward is pa_forward_ex with flags 0).
+ *
+ *   PA_FORWARD_SHARED_BLOCKS  some physical blocks appear in more than one
+ *       row's table (prefix caching: blocks with a reference count above one,
+ *       section "Prefix Caching"). KV is then read through the caches so the
+ *       shared blocks are served from them; without the flag V is read with
+ *       streaming (nontemporal) loads, the faster choice for blocks read once.
+ *       Either way the results are identical.
+ *
+ * Unknown flag bits return PA_ERR_UNSUPPORTED.
+ */
+#define PA_FORWARD_SHARED_BLOCKS 1u
+
+int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                  int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                  size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
  * Synchronous check of the device-resident metadata that the hot path
  * trusts (for tests and debugging; copies to the host and waits on
  * `stream`). Checks: query_start_loc starts at 0, never decreases and ends at

@@ -21,6 +21,7 @@ __all__ = ["cache_write", "forward", "forward_workspace_bytes", "validate_inputs
            "profile_begin", "profile_end", "PaError", "BLOCK_SIZE", "KERNEL_CLASSES"]
 
 BLOCK_SIZE = 16
+FORWARD_SHARED_BLOCKS = 1  # PA_FORWARD_SHARED_BLOCKS
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
 _lib = None
@@ -41,6 +42,9 @@ SIGNATURES = {
     "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32,
                                   _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
+    "pa_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
+                                     _I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ,
+                                     ctypes.c_uint32, _P]),
     "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                           _I32, _I32, _P]),
     "pa_profile_begin": (ctypes.c_int, []),
@@ -169,12 +173,15 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
             scale: float, out: Optional[torch.Tensor] = None,
             max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
-            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+            workspace: Optional[torch.Tensor] = None,
+            shared_blocks: bool = False) -> torch.Tensor:
     """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
     paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
     ``max_seq_len`` are optional host upper bounds that shrink the launch
     grids; ``workspace`` (uint8, on the device, zero-filled before its first
-    use) is taken from a per-device cache when omitted."""
+    use) is taken from a per-device cache when omitted. ``shared_blocks``
+    tells the library that some blocks appear in several rows' tables
+    (prefix caching); results are the same either way."""
     lib = load_library()
     _dev_tensor("q", q, torch.bfloat16, 3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -200,12 +207,12 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         workspace = _workspace(q.device, need)
     elif workspace.device != q.device:
         raise ValueError("workspace must be on q's device")
-    _check(lib.pa_forward(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                          block_table.data_ptr(), seq_lens.data_ptr(),
-                          query_start_loc.data_ptr(), float(scale), out.data_ptr(), T, S, Hq,
-                          Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
-                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          _stream(q)))
+    _check(lib.pa_forward_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                             block_table.data_ptr(), seq_lens.data_ptr(),
+                             query_start_loc.data_ptr(), float(scale), out.data_ptr(), T, S, Hq,
+                             Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             FORWARD_SHARED_BLOCKS if shared_blocks else 0, _stream(q)))
     return out
 
 

@@ -39,18 +39,27 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)float_to_bf16_bits(lo) | ((uint32_t)float_to_bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// {packed bf16 hi parts, packed bf16 residuals} of two floats: x ~= hi + lo
+// to about 2^-17 relative, so a PV product run as two bf16 MFMAs keeps the
+// weights' precision.
+__device__ __forceinline__ u32x2 split_pack_bf16x2(float a, float b) {
+  const uint32_t hi = pack_bf16x2(a, b);
+  const float ha = __uint_as_float(hi << 16);
+  const float hb = __uint_as_float(hi & 0xffff0000u);
+  return u32x2{hi, pack_bf16x2(a - ha, b - hb)};
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Split p into bf16 parts with p ~= hi + lo to about 2^-17 relative: the PV
-// product then runs as two bf16 MFMAs and keeps the weights' precision.
-__device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) {
-  hi = float_to_bf16_bits(p);
-  lo = float_to_bf16_bits(p - bf16_bits_to_float(hi));
-}
 
 // gfx950 LDS transpose read. Within each 16-lane block, lane i receives
 // element e = the 16-bit value at offset (i % 4) of the 8 bytes addressed by

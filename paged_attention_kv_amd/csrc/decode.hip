@@ -108,7 +108,7 @@ __device__ __forceinline__ void merge_head_quad(const float* __restrict__ ws_o,
   *(u32x2*)(out + out_off + 4 * d4) = pr;
 }
 
-template <int D, int NBUF>
+template <int D, int NBUF, bool kStreamV>
 __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
@@ -170,6 +170,10 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
     const uint16_t* vbase = v_cache + (int64_t)g * D;
 
     // Loads block min(j, nblk-1): always issued, so the wait counts stay exact.
+    // Unless blocks are shared between rows, V goes through nontemporal
+    // (streaming) loads: each V load covers whole rows and is read once, and
+    // measured faster that way. K keeps plain loads: two of its loads cover
+    // the two halves of one 128-byte line, which streaming loads re-fetch.
     auto load_block = [&](int j, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
       const int jj = min(j, nblk - 1);
       const int64_t blk = __builtin_amdgcn_readlane(my_blk, jj);
@@ -182,7 +186,8 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
         const int idx = c * kWave + lane;
         const int row = idx / (D / 8);
         const int col8 = idx % (D / 8);
-        vv[c] = *(const u32x4*)(vbase + boff + row * kv_row + col8 * 8);
+        const u32x4* vp = (const u32x4*)(vbase + boff + row * kv_row + col8 * 8);
+        vv[c] = kStreamV ? __builtin_nontemporal_load(vp) : *vp;
       }
     };
 
@@ -219,16 +224,16 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
         for (int mi = 0; mi < Sh::kDTiles; ++mi) o[mi] *= alpha;
         m = mn;
       }
-      i16x4 phi, plo;
+      float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sv[r] - m);
-        lsum += p;
-        uint16_t h, l;
-        split_bf16(p, h, l);
-        phi[r] = (short)h;
-        plo[r] = (short)l;
+        p[r] = fast_exp2(sv[r] - m);
+        lsum += p[r];
       }
+      const u32x2 s01 = split_pack_bf16x2(p[0], p[1]);
+      const u32x2 s23 = split_pack_bf16x2(p[2], p[3]);
+      const i16x4 phi = __builtin_bit_cast(i16x4, u32x2{s01[0], s23[0]});
+      const i16x4 plo = __builtin_bit_cast(i16x4, u32x2{s01[1], s23[1]});
       wave_lds_fence();
       // A operand V^T[d = 16*mi + hl][token 4*grp + r] by transpose reads.
       const uint16_t* vrow = vl + (4 * grp + hl / 4) * Sh::kLdsRow + 4 * (hl % 4);
@@ -381,14 +386,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   for (int e = 0; e < kPer; ++e) op[lane + kWave * e] = float_to_bf16_bits(acc[e] * inv);
 }
 
-template <int D, int NBUF>
+template <int D, int NBUF, bool kStreamV>
 hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
   const int waves = a.num_kv_heads < kMaxWavesPerGroup ? a.num_kv_heads : kMaxWavesPerGroup;
   const int groups = (a.num_kv_heads + waves - 1) / waves;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   dim3 grid(p.num_parts_max, a.num_seqs, groups);
   profile_begin(PA_KERNEL_DECODE, stream);
-  hipLaunchKernelGGL((decode_partition_kernel<D, NBUF>), grid, dim3(waves * kWave), 0, stream,
+  hipLaunchKernelGGL((decode_partition_kernel<D, NBUF, kStreamV>), grid, dim3(waves * kWave), 0,
+                     stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                      (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                      (uint16_t*)a.out, p.ws_o, p.ws_ml, p.counters, scale_log2, a.num_q_heads,
@@ -417,15 +423,18 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
   if (p.part_tokens <= 0 || p.part_tokens % kBlock || p.part_tokens > kMaxPartTokens)
     return hipErrorInvalidValue;
   const int nbuf = p.prefetch;
+  const bool sv = p.stream_v;
+#define PA_DECODE_CASE(DD)                                                            \
+  if (nbuf <= 2) return sv ? launch_decode_nb<DD, 2, true>(a, p, stream)             \
+                           : launch_decode_nb<DD, 2, false>(a, p, stream);           \
+  if (nbuf == 3) return sv ? launch_decode_nb<DD, 3, true>(a, p, stream)             \
+                           : launch_decode_nb<DD, 3, false>(a, p, stream);           \
+  return sv ? launch_decode_nb<DD, 4, true>(a, p, stream)                            \
+            : launch_decode_nb<DD, 4, false>(a, p, stream);
   switch (a.head_size) {
-    case 64:
-      if (nbuf <= 2) return launch_decode_nb<64, 2>(a, p, stream);
-      if (nbuf == 3) return launch_decode_nb<64, 3>(a, p, stream);
-      return launch_decode_nb<64, 4>(a, p, stream);
-    case 128:
-      if (nbuf <= 2) return launch_decode_nb<128, 2>(a, p, stream);
-      if (nbuf == 3) return launch_decode_nb<128, 3>(a, p, stream);
-      return launch_decode_nb<128, 4>(a, p, stream);
+    case 64: { PA_DECODE_CASE(64) }
+    case 128: { PA_DECODE_CASE(128) }
+#undef PA_DECODE_CASE
     default: return hipErrorInvalidValue;
   }
 }

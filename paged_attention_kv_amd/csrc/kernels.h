@@ -38,6 +38,7 @@ struct DecodePlan {
   int32_t num_parts_max;  // partitions per row (grid x; workspace stride)
   int32_t prefetch;       // register ring depth in 16-token blocks (2..4)
   bool fused;             // last-arriving workgroup merges (else a combine kernel)
+  bool stream_v;          // V through nontemporal loads (blocks not shared)
   float* ws_o;            // [S][num_parts_max][Hq][D] unnormalised partial outputs
   float* ws_ml;           // [S][num_parts_max][Hq][2] reference max (log2 units) and sum
   int32_t* counters;      // [S][decode_groups(Hkv)] arrival counters, zero between calls

@@ -57,7 +57,7 @@ int32_t resolved_max_seq_len(int32_t max_blocks_per_seq, int32_t hint) {
 }
 
 // Tokens per split-K partition of a decode row: the largest size that still
-// yields at least two workgroups per CU of a 256-CU part when every row is as
+// yields at least one workgroup per CU of a 256-CU part when every row is as
 // long as the longest. PA_DECODE_PART_TOKENS overrides it (multiple of 16 in
 // [128, 1024]) for tuning sweeps.
 int32_t choose_part_tokens(int32_t num_seqs, int32_t max_len) {
@@ -68,7 +68,7 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t max_len) {
   if (env) return env;
   for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
     const int64_t items = (int64_t)num_seqs * ((max_len + p - 1) / p);
-    if (items >= 512) return p;
+    if (items >= 256) return p;
   }
   return kMinPartTokens;
 }
@@ -77,9 +77,9 @@ bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 ||
 
 // Register ring depth of the decode kernel (blocks in flight per wave);
 // PA_DECODE_PREFETCH overrides it for tuning sweeps.
-int32_t decode_prefetch() {
-  static const int v = env_int("PA_DECODE_PREFETCH", 2, 4, 3);
-  return v;
+int32_t decode_prefetch(int32_t head_size) {
+  static const int v = env_int("PA_DECODE_PREFETCH", 2, 4, 0);
+  return v ? v : (head_size <= 64 ? 3 : 2);
 }
 
 // Rows with at most this many partitions are merged by their last-arriving
@@ -179,7 +179,22 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
                int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
                size_t workspace_bytes, void* stream) {
+  return pa_forward_ex(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out,
+                       num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                       max_blocks_per_seq, num_blocks, max_query_len_hint, max_seq_len_hint,
+                       workspace, workspace_bytes, 0u, stream);
+}
+
+int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                  int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                  size_t workspace_bytes, uint32_t flags, void* stream) {
   g_last_error.clear();
+  if (flags & ~(uint32_t)PA_FORWARD_SHARED_BLOCKS)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_ex: unknown flags 0x%x", flags);
   if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
     return fail(PA_ERR_SHAPE, "pa_forward: a size is out of range (T=%d S=%d Hq=%d Hkv=%d D=%d "
@@ -254,7 +269,8 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
   pa::DecodePlan dp;
   dp.part_tokens = w.part_tokens;
   dp.num_parts_max = (a.max_seq_len + w.part_tokens - 1) / w.part_tokens;
-  dp.prefetch = decode_prefetch();
+  dp.prefetch = decode_prefetch(head_size);
+  dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
   dp.fused = dp.num_parts_max > 1 && dp.num_parts_max <= fused_max_parts() &&
              (int64_t)num_seqs * pa::decode_groups(num_kv_heads) <= kCounterSlots;
   dp.ws_o = (float*)(ws + w.off_o);

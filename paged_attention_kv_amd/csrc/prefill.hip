@@ -119,6 +119,10 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   }
 }
 
+// LDS chunk swizzles of the K and V tiles (see the kernel).
+__device__ __forceinline__ int swz_k(int r) { return r & 7; }
+__device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
+
 template <int D, int G, bool SPLIT>
 __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -129,20 +133,21 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
     int32_t MB, int32_t tile_bound) {
   constexpr int BQ = kRowsPerWG / G;          // query tokens per tile
   constexpr int BN = kKeysPerTile;            // keys per iteration
-  constexpr int RSK = D + 8;                  // padded LDS row of K (elements): row reads
-                                              // of 8 lanes hit 8 distinct bank quads
-  constexpr int RSV = D + 16;                 // padded LDS row of V: the 4 rows of a
-                                              // transpose read sit 8 banks apart
+  constexpr int RB = D * 2;                   // bytes of one K or V row (unpadded)
   constexpr int KC = D / 32;                  // QK MFMAs per 16x16 S tile
   constexpr int DT = D / 16;                  // PV output tiles along d
   constexpr int NS = BN / 16;                 // 16-key sub-tiles per tile
   constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
-  constexpr int CPT = BN * CPR / kPrefillThreads;  // chunks per thread per tile
-  static_assert(CPT * kPrefillThreads == BN * CPR, "tile must split evenly");
+  constexpr int NDMA = BN * RB / 1024 / 4;    // 1 KiB load-to-LDS ops per wave per tile
+  static_assert(NDMA * 4 * 1024 == BN * RB, "tile must split evenly");
 
-  // Two stages: the tile being computed and the one being filled.
-  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * RSK];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * RSV];
+  // Two stages (the tile being computed and the one being filled), rows
+  // unpadded; 16-byte chunk c of row r sits at chunk c ^ swz(r) so that both
+  // the row reads of the QK operand (8 rows per phase, K) and the transpose
+  // reads of the PV operand (4 rows per 16-lane block, V) are bank-conflict
+  // free.
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[2][BN * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[2][BN * RB];
 
   // One (sequence, query tile, KV head) task.
   auto run_tile = [&](const int s, const int q0, const int g) {
@@ -192,29 +197,42 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   float lsum[2] = {0.f, 0.f};
 
   const int32_t* table = block_table + (int64_t)s * MB;
-  u32x4 kr[CPT], vr[CPT];
-  // Keys at or past kv_end load key kv_end-1 instead: finite data that the
-  // mask removes (a zero weight times a finite value), never a stale slot.
-  auto load_tile = [&](int kt) {
+  const int last_blk = (kv_end - 1) / kBlock;  // last block any row reads
+  constexpr int kTileBlocks = BN / kBlock;     // 16-token blocks per key tile
+  // Block ids of key tile kt: lane b < kTileBlocks holds entry kt*4 + b
+  // (clamped to the last block read), fetched one iteration ahead.
+  auto tile_ids = [&](int kt) {
+    return lane < kTileBlocks ? table[min(kt * kTileBlocks + lane, last_blk)] : 0;
+  };
+  // Tile kt straight from HBM/L2 into LDS stage `stage`: load op j of wave w
+  // fills LDS bytes (j*4 + w)*1024 .. +1024, lane l the 16 bytes at l*16,
+  // i.e. row r, physical chunk pc; it fetches logical chunk pc ^ swz(r) of
+  // key kt*64 + r. The rows of one op lie in one 16-key block (wave-uniform
+  // table id).
+  auto dma_tile = [&](int kt, int stage, int ids) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int cidx = j * kPrefillThreads + tid;
-      const int key = min(kt * BN + cidx / CPR, kv_end - 1);
-      const int col8 = cidx % CPR;
-      const int64_t blk = table[key / kBlock];
-      const int64_t off = (blk * kBlock + key % kBlock) * kv_row + (int64_t)g * D + col8 * 8;
-      kr[j] = *(const u32x4*)(k_cache + off);
-      vr[j] = *(const u32x4*)(v_cache + off);
+    for (int j = 0; j < NDMA; ++j) {
+      const int p = (j * 4 + w) * 1024 + lane * 16;
+      const int r = p / RB;
+      const int pc = (p % RB) / 16;
+      const int64_t blk = __builtin_amdgcn_readlane(ids, ((j * 4 + w) * 1024 / RB) / kBlock);
+      const int64_t row = (blk * kBlock + r % kBlock) * kv_row + (int64_t)g * D;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(k_cache + row + (pc ^ swz_k(r)) * 8),
+          (__attribute__((address_space(3))) void*)(&ks[stage][(j * 4 + w) * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(v_cache + row + (pc ^ swz_v(r)) * 8),
+          (__attribute__((address_space(3))) void*)(&vs[stage][(j * 4 + w) * 1024]), 16, 0, 0);
     }
   };
-  auto store_tile = [&](int stage) {
+  // Rows of tile kt at or past kv_end came from a clamped or partly used
+  // block: zero their V (each thread the bytes it loaded itself, after its
+  // own loads completed), so a zero weight never meets a stale value.
+  auto zero_tail = [&](int kt, int stage) {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const int cidx = j * kPrefillThreads + tid;
-      const int key = cidx / CPR;
-      const int col8 = cidx % CPR;
-      *(u32x4*)(&ks[stage][key * RSK + col8 * 8]) = kr[j];
-      *(u32x4*)(&vs[stage][key * RSV + col8 * 8]) = vr[j];
+    for (int j = 0; j < NDMA; ++j) {
+      const int p = (j * 4 + w) * 1024 + lane * 16;
+      if (kt * BN + p / RB >= kv_end) *(u32x4*)(&vs[stage][p]) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -222,8 +240,8 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   // split: P enters PV as bf16 hi + lo parts (rows with few visible keys).
   auto compute_tile = [&](int kt, int stage, bool masked, auto split_tag) {
     constexpr bool kSplit = decltype(split_tag)::value;
-    const uint16_t* kst = ks[stage];
-    const uint16_t* vst = vs[stage];
+    const uint8_t* kst = ks[stage];
+    const uint8_t* vst = vs[stage];
     f32x4 st[2][NS];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -233,7 +251,8 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
     for (int n = 0; n < NS; ++n) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + (n * 16 + hl) * RSK + 32 * i + 8 * grp));
+        const int r = n * 16 + hl;
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + r * RB + ((4 * i + grp) ^ swz_k(r)) * 16));
         st[0][n] = mfma_16x16x32(a, qv[0][i], st[0][n]);
         st[1][n] = mfma_16x16x32(a, qv[1][i], st[1][n]);
       }
@@ -296,14 +315,13 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         if constexpr (kSplit) {
-          uint16_t h[8], l[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) split_bf16(st[mt][2 * kp + e / 4][e % 4], h[e], l[e]);
           u32x4 hv, lv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            hv[e] = (uint32_t)h[2 * e] | ((uint32_t)h[2 * e + 1] << 16);
-            lv[e] = (uint32_t)l[2 * e] | ((uint32_t)l[2 * e + 1] << 16);
+            const u32x2 hl2 = split_pack_bf16x2(st[mt][2 * kp + e / 2][2 * (e % 2)],
+                                                st[mt][2 * kp + e / 2][2 * (e % 2) + 1]);
+            hv[e] = hl2[0];
+            lv[e] = hl2[1];
           }
           pb[mt] = as_bf16x8(hv);
           pl[mt] = as_bf16x8(lv);
@@ -315,11 +333,14 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
           pb[mt] = as_bf16x8(hv);
         }
       }
-      const uint16_t* vrow = vst + (kp * 32 + 4 * grp + hl / 4) * RSV + 4 * (hl % 4);
+      const int r0 = kp * 32 + 4 * grp + hl / 4;  // rows r0 and r0 + 16 share swz_v
+      const uint8_t* vrow0 = vst + r0 * RB + ((hl % 4) & 1) * 8;
+      const uint8_t* vrow1 = vrow0 + 16 * RB;
 #pragma unroll
       for (int mi = 0; mi < DT; ++mi) {
-        const i16x4 a0 = lds_read_tr16(vrow + 16 * mi);
-        const i16x4 a1 = lds_read_tr16(vrow + 16 * RSV + 16 * mi);
+        const int c = (2 * mi + (hl % 4) / 2) ^ swz_v(r0);
+        const i16x4 a0 = lds_read_tr16((const uint16_t*)(vrow0 + c * 16));
+        const i16x4 a1 = lds_read_tr16((const uint16_t*)(vrow1 + c * 16));
         const bf16x8 av = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         o[0][mi] = mfma_16x16x32(av, pb[0], o[0][mi]);
@@ -333,13 +354,21 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   };
 
 
-  load_tile(0);
-  store_tile(0);
-  if (ntiles > 1) load_tile(1);
+  dma_tile(0, 0, tile_ids(0));
+  int ids_next = tile_ids(1);
   for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // stage kt%2 is filled; every wave is done with tile kt-1
-    if (kt + 1 < ntiles) store_tile((kt + 1) & 1);
-    if (kt + 2 < ntiles) load_tile(kt + 2);
+    // This wave's loads into stage kt%2 are complete (the barrier's release
+    // waits for all of them), every wave's are once all have arrived, and
+    // every wave is done reading tile kt-1 from stage (kt+1)%2.
+    __syncthreads();
+    if ((kt + 1) * BN > kv_end) {
+      zero_tail(kt, kt & 1);
+      __syncthreads();
+    }
+    if (kt + 1 < ntiles) {
+      dma_tile(kt + 1, (kt + 1) & 1, ids_next);
+      ids_next = tile_ids(kt + 2);
+    }
     const bool masked = (kt + 1) * BN - 1 > first_lim;
     // Tiles whose rows see at most kSplitKeys keys (SPLIT) keep P to about
     // 2^-17 (hi + lo): few weights carry each output there, and bf16

@@ -93,6 +93,9 @@ def test_forward_rejects_bad_arguments(lib):
     assert fw(lib, wsb=16) == -5
     assert "workspace" in pa.last_error()
     assert fw(lib, T=0) == 0              # empty batch: no launch
+    # unknown option flags are rejected before anything else happens
+    assert lib.pa_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 8, 2, 32, 4, 64, 16,
+                             4, 64, 0, 0, FAKE, 1 << 30, 6, None) == -3
 
 
 def test_validate_rejects_null_before_touching_the_device(lib):
@@ -115,3 +118,9 @@ def test_workspace_sizes_for_the_named_workloads(lib, i):
     n2 = pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads, s.num_kv_heads,
                                     s.head_size, s.max_blocks_per_seq, max(s.seq_lens))
     assert n2 <= n
+
+
+def test_profile_with_no_launches_is_empty(lib):
+    # begin/end with nothing launched in between touches no HIP call
+    pa.profile_begin()
+    assert pa.profile_end() == {}

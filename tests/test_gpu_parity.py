@@ -158,11 +158,12 @@ def test_long_decode_sampled_rows():
     assert_close(out[rows], want, "long decode")
 
 
-def test_prefix_shared_sampled_rows():
+@pytest.mark.parametrize("shared_flag", [True, False])
+def test_prefix_shared_sampled_rows(shared_flag):
     spec = wl.config(5)
-    banner("forward workload 5 (prefix-shared decode), 16 rows")
+    banner(f"forward workload 5 (prefix-shared decode), 16 rows, shared_blocks={shared_flag}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case).cpu()
+    out = write_and_forward(case, shared_blocks=shared_flag).cpu()
     pick = sorted(random.Random(5).sample(range(256), 14) + [0, 255])
     rows, want = oracle_rows(case, pick)
     assert_close(out[rows], want, "prefix shared")
@@ -317,3 +318,17 @@ def test_workspace_shared_by_calls_of_different_shapes():
         pick = list(range(0, spec.num_seqs, max(1, spec.num_seqs // 6)))
         r, want = oracle_rows(case, pick)
         assert_close(out.cpu()[r], want, spec.name)
+
+
+def test_kernel_timing_records_each_launch_class():
+    spec = wl.custom("prof", 32, 8, 128, rows=[(1, 3000), (40, 100), (1, 20)], seed=49)
+    case = wl.make_case(spec, device=DEV)
+    pa.profile_begin()
+    out = write_and_forward(case)
+    per = pa.profile_end()
+    assert per["cache_write"][0] == 1 and per["decode"][0] == 1 and per["prefill"][0] == 1
+    assert per["plan"][0] == 1 and per["prefill_short"][0] == 1
+    assert all(ms > 0 for _, ms in per.values())
+    # timing does not change results
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "profiled forward")
