@@ -197,7 +197,7 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key: str):
+def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
     for a copy of known size), or None when the summary is missing or was
@@ -210,10 +210,11 @@ def measured_traffic(kernel_key: str):
         return None
     if rec.get("decode_src_sha256_16") != decode_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
-    if not k or "write_bytes" not in k:
-        return None
-    return int(k["read_bytes"] + k["write_bytes"])
+    for key, k in rec.get("kernels", {}).items():
+        name, _, wl = key.partition(" @ ")
+        if kernel in name and wl.startswith(workload) and "write_bytes" in k:
+            return int(k["read_bytes"] + k["write_bytes"])
+    return None
 
 
 def cpu_baseline(spec, budget_s: float = 12.0):
@@ -360,11 +361,10 @@ def main(argv=None):
             "tokens": 64, "kv_bytes_per_step": d["bytes_step"],
             "block_table_rotations": d["rotations"],
             "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
-        line["roofline"] = {"bound": "hbm", "kernel": "decode_partition_kernel<64, 3, true>",
+        line["roofline"] = {"bound": "hbm", "kernel": "decode_kernel<64, 2, true>",
                             "achieved": round(d["kernel_gbs"], 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic(
-                                "decode_partition_kernel<64, 3, true> @ decode (64 x U[512,2048], D 64)"),
+                            "traffic": measured_traffic("decode_kernel<64, 2, true>", "decode ("),
                             "avg_launch_us": round(d["ms_decode_kernel"] * 1e3, 3),
                             "algorithmic_bytes_per_launch": d["bytes_fwd"],
                             "forward_kernels_us_per_step": round(d["ms_fwd"] * 1e3, 3),

@@ -86,11 +86,10 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    int64_t num_blocks, int32_t block_size, void* stream);
 
 /*
- * Workspace bytes pa_forward needs for these sizes: a fixed 256 KiB region
- * of split-K arrival counters at the start (never written with anything
- * else, so one zero-filled workspace can serve calls of any shape), then the
- * split-K partial results of decode rows and the work list of prefill tiles.
- * Depends only on its arguments; returns 0 if an argument is out of range.
+ * Workspace bytes pa_forward needs for these sizes: the split-K partial
+ * results of decode rows and the work list of prefill tiles. Depends only on
+ * its arguments; returns 0 if an argument is out of range or the sizes are
+ * not supported (more than 65535 split-K partitions of 128 tokens per row).
  * max_seq_len_hint <= 0 means "unknown" (max_blocks_per_seq * 16 is used).
  */
 size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
@@ -117,10 +116,9 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  *                    are used). A hint below the true maximum is a contract
  *                    violation (rows past it are not computed).
  *   workspace        device, >= pa_forward_workspace_bytes(...) bytes,
- *                    16-byte aligned, zero-filled before its first use: it
- *                    holds split-K arrival counters that every call leaves at
- *                    zero again, the rest is scratch. Calls that share a
- *                    workspace must be ordered on one stream.
+ *                    16-byte aligned, any contents: scratch that each call
+ *                    writes before it reads. Calls that share a workspace
+ *                    must be ordered on one stream.
  *
  * Query row i of sequence s (i < q_len = qsl[s+1] - qsl[s]) sits at position
  * c + i with c = seq_lens[s] - q_len and attends to keys 0..c+i of its own
@@ -129,10 +127,10 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * path (split-K over the context), rows with q_len > 1 the prefill path.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
  * Tuning overrides, read once per process (for sweeps; out-of-range values
- * are ignored): PA_DECODE_PART_TOKENS (split-K partition, 128..1024, a
- * multiple of 16), PA_DECODE_PREFETCH (blocks in flight per wave, 2..4),
- * PA_DECODE_FUSED_MAX (rows with at most this many partitions are merged by
- * their last workgroup, 0..16; 0 = always use the combine kernel).
+ * are ignored): PA_DECODE_PART_TOKENS (tokens per decode partition, a
+ * multiple of 16, at least 128), PA_DECODE_WAVES (waves per decode
+ * workgroup, 1..16 within the head size's limit), PA_DECODE_PREFETCH (blocks
+ * in flight per wave at head_size 64, 2..3).
  * Requires block_size == 16, head_size in {64, 128}, num_q_heads /
  * num_kv_heads in {1, 2, 4, 8, 16}. Caller contract: 0 <= q_len <= seq_len
  * <= max_blocks_per_seq * 16 and the first ceil(seq_len / 16) table entries

@@ -162,9 +162,7 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        # zero-filled once: the split-K arrival counters must start at zero
-        # (the library leaves them zero after every call)
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -178,8 +176,8 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
     paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
     ``max_seq_len`` are optional host upper bounds that shrink the launch
-    grids; ``workspace`` (uint8, on the device, zero-filled before its first
-    use) is taken from a per-device cache when omitted. ``shared_blocks``
+    grids; ``workspace`` (uint8, on the device, any contents) is taken from a
+    per-device cache when omitted. ``shared_blocks``
     tells the library that some blocks appear in several rows' tables
     (prefix caching); results are the same either way."""
     lib = load_library()

@@ -101,17 +101,6 @@ __device__ __forceinline__ float sum_across_groups(float v) {
   return a + b;
 }
 
-// Device-coherent 32-bit store and load (agent scope, relaxed): the store
-// writes through this XCD's L2 and the load does not hit a stale line in it,
-// so workgroups on different XCDs can hand data over without flushing or
-// invalidating whole caches.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Orders this wave's LDS writes before its later LDS reads (and the reverse)
 // without a workgroup barrier: LDS instructions of one wave execute in order,
 // so only the compiler has to be kept from moving them.

@@ -1,6 +1,6 @@
 // Decode rows of the flattened batch (one query token per sequence): paged
-// attention over the sequence's whole context, split over the context into
-// partitions whose partial softmax states are then merged.
+// attention over the sequence's whole context, optionally split over the
+// context into partitions whose partial softmax states are then merged.
 //
 // What is computed follows the pages "Inside vLLM: Anatomy of a
 // High-Throughput LLM Inference System": section "Scheduler" (decode requests
@@ -8,10 +8,11 @@
 // bandwidth; blocks hold 16 tokens) and section "Run forward pass" (block
 // tables index the paged KV memory; each sequence sees only its own tokens).
 //
-// Work decomposition (gfx950): a workgroup is one (sequence, partition) and
-// holds one wave per KV head, so a workgroup streams whole 16-token blocks
-// (all heads of a block are contiguous in [NB, 16, Hkv, D]). Each wave keeps
-// the G query heads of its KV head in MFMA operands:
+// Work decomposition (gfx950): a workgroup is one (sequence, KV head,
+// partition of the context) and holds W waves that take the partition's
+// 16-token blocks in turn (wave w: blocks w, w+W, ...), so that one CU keeps
+// many blocks in flight even when a row is short. Each wave keeps the G query
+// heads of the KV head in MFMA operands:
 //   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]   (16x16x32 bf16 MFMA,
 //                                                          K straight from HBM)
 //   O^T[D x 16 heads]       += V^T[D x 16] . P^T[16 x 16] (16x16x16 bf16 MFMA,
@@ -20,7 +21,8 @@
 // the B operand layout of the second product, so P never leaves registers.
 // Blocks stream through a ring of NBUF register buffers whose loads are
 // issued unconditionally (indices clamped), so the compiler's wait counts
-// only ever wait for the block being consumed.
+// only ever wait for the block being consumed. At the end the W partial
+// softmax states are merged through LDS.
 //
 // Softmax: scores are kept in log2 units against a per-head reference max m.
 // m is only recomputed (one max across the four 16-lane groups) and the
@@ -28,10 +30,13 @@
 // between, weights are exp2(s - m) <= 2^kLazy, which bf16 hi+lo parts and the
 // fp32 accumulators carry without loss.
 //
-// Split-K merge: a partition that is not its row's only one writes
-// (m, l, o) to the workspace. With `fused`, the last workgroup of a row to
-// finish (an atomic counter per row, reset by that workgroup) merges the
-// partitions itself; otherwise a separate combine kernel does it.
+// Split-K: when rows x KV heads alone would leave CUs idle, rows are split
+// into partitions; a partition that is not its row's only one writes its
+// merged (m, l, o) to the workspace and a combine kernel merges the
+// partitions. (Merging in the last-arriving workgroup instead measured slower
+// on this chip: a row's partitions run on several XCDs, whose L2s are not
+// coherent with each other, so the hand-over costs three memory round trips
+// at the tail, more than the kernel boundary it saves.)
 #include <math.h>
 
 #include "common.h"
@@ -41,9 +46,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kMaxWavesPerGroup = 8;
-constexpr int kMaxPartTokens = 64 * kBlock;  // one table entry per lane
-constexpr float kLazy = 8.0f;                // log2 of the largest unnormalised weight
+constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
 
 template <int D>
 struct DecodeShape {
@@ -53,8 +56,18 @@ struct DecodeShape {
   // Padded LDS row of V (elements): rows 16B aligned, and consecutive rows 8
   // banks apart so the four rows of one transpose read do not collide.
   static constexpr int kLdsRow = D + 16;
-  static constexpr int kLdsWave = kBlock * kLdsRow;
+  static constexpr int kLdsWave = kBlock * kLdsRow;  // elements per wave
+  // Merge stage (fp32), heads handled per pass: o rows of D + 4 floats.
+  // W * 8 * (D + 4) * 4 + W * 8 * 8 bytes fit in the W V slices.
+  static constexpr int kMergeHeads = 8;
+  static constexpr int kMergeRow = D + 4;
+  static_assert(kMergeHeads * (kMergeRow * 4 + 8) <= kLdsWave * 2, "merge stage fits in LDS");
 };
+
+// Most waves per decode workgroup: as many as fit on a CU at the kernel's
+// register use (<= 128 VGPRs: 4 waves per SIMD; <= 168: 3).
+template <int D, int NBUF>
+constexpr int max_waves() { return (D == 64 && NBUF == 2) ? 16 : 12; }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -67,73 +80,38 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Merge the np <= kMaxFusedParts partitions of one query head of a decode
-// row: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,
-// summed in partition order. All loads are issued before the first use, so
-// the merge costs one memory round trip. Produces the four d of quad d4.
-constexpr int kMaxFusedParts = 16;
-template <int D>
-__device__ __forceinline__ void merge_head_quad(const float* __restrict__ ws_o,
-                                                const float* __restrict__ ws_ml,
-                                                uint16_t* __restrict__ out, int64_t row0,
-                                                int32_t Hq, int np, int64_t out_off, int d4) {
-  float mv[kMaxFusedParts], lv[kMaxFusedParts];
-  f32x4 ov[kMaxFusedParts];
-#pragma unroll
-  for (int p = 0; p < kMaxFusedParts; ++p) {
-    if (p < np) {
-      const int64_t r = row0 + (int64_t)p * Hq;
-      mv[p] = load_coherent(ws_ml + r * 2);
-      lv[p] = load_coherent(ws_ml + r * 2 + 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ov[p][e] = load_coherent(ws_o + r * D + 4 * d4 + e);
-    }
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < kMaxFusedParts; ++p)
-    if (p < np) M = fmaxf(M, mv[p]);
-  float W = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int p = 0; p < kMaxFusedParts; ++p) {
-    if (p < np) {
-      const float w = fast_exp2(mv[p] - M);
-      W += w * lv[p];
-      acc += w * ov[p];
-    }
-  }
-  const float inv = 1.0f / W;
-  u32x2 pr = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *(u32x2*)(out + out_off + 4 * d4) = pr;
-}
-
 template <int D, int NBUF, bool kStreamV>
-__global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_kernel(
+__global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int32_t* __restrict__ counters, float scale_log2, int32_t Hq, int32_t Hkv, int32_t G,
-    int32_t MB, int32_t part_tokens, int32_t num_parts_max, int32_t waves_per_group,
-    int32_t fused) {
+    float scale_log2, int32_t Hq, int32_t Hkv, int32_t G, int32_t MB, int32_t part_tokens,
+    int32_t num_parts_max) {
   using Sh = DecodeShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kMaxWavesPerGroup * Sh::kLdsWave];
-  __shared__ int32_t last_flag;
+  // W V slices of kLdsWave elements while streaming; the merge stage after.
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  const int s = blockIdx.y;
-  const int part = blockIdx.x;
-  const int g = blockIdx.z * waves_per_group + w;
-  const bool active = g < Hkv;  // wave-uniform; idle waves still meet the barriers
-  // This partition's block ids (lane j: entry part*part_tokens/16 + j), read
-  // before the row's length is known so the two loads overlap; the index is
-  // kept inside the row, and lanes past the partition are never used.
-  const int b_begin = part * (part_tokens / kBlock);
-  const int my_blk = (lane < part_tokens / kBlock && b_begin + lane < MB)
-                         ? block_table[(int64_t)s * MB + b_begin + lane] : 0;
-  // Workgroup-uniform exits, all before any barrier.
+  // The wave index is uniform across the wave; saying so keeps the block
+  // loop and the table reads on scalar registers.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int W = blockDim.x / kWave;
+  // Rows vary fastest in the grid: consecutive workgroups are dealt to the
+  // XCDs in turn, so the work of every partition index and head spreads
+  // over all XCDs.
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const int part = blockIdx.z;
+  // Block ids of this wave (lane k: partition block w + k*W), read before
+  // the row's length is known so the loads overlap; the index is kept inside
+  // the row, and lanes past the wave's blocks are never used.
+  const int bpp = part_tokens / kBlock;
+  const int b_begin = part * bpp;
+  const int jb = w + lane * W;
+  const int my_blk = (jb < bpp && b_begin + jb < MB)
+                         ? block_table[(int64_t)s * MB + b_begin + jb] : 0;
+  // Workgroup-uniform exits (before any barrier).
   const int t0 = qsl[s];
   if (qsl[s + 1] - t0 != 1) return;  // not a decode row
   const int L = seq_lens[s];
@@ -142,10 +120,10 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
   const int tok_end = min(L, tok_begin + part_tokens);
   const int nparts = (L + part_tokens - 1) / part_tokens;
   const int nblk = (tok_end + kBlock - 1) / kBlock - b_begin;
+  const int nmine = nblk > w ? (nblk - 1 - w) / W + 1 : 0;  // blocks of this wave
 
   const int hl = lane & 15;   // head within the group (MFMA column)
   const int grp = lane >> 4;  // 16-lane group
-  const int qh = g * G + hl;
   const int64_t kv_row = (int64_t)Hkv * D;  // elements between consecutive tokens of a block
 
   f32x4 o[Sh::kDTiles];
@@ -154,11 +132,11 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
   float m = -INFINITY;
   float lsum = 0.f;
 
-  if (active) {
+  if (nmine > 0) {
     // Q^T as the B operand: lane holds head hl, d = 32*i + 8*grp + e.
     bf16x8 qv[Sh::kKChunks];
     {
-      const u32x4* qp = (const u32x4*)(q + ((int64_t)t0 * Hq + qh) * D) + grp;
+      const u32x4* qp = (const u32x4*)(q + ((int64_t)t0 * Hq + g * G + hl) * D) + grp;
 #pragma unroll
       for (int i = 0; i < Sh::kKChunks; ++i) {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -169,14 +147,14 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
     const uint16_t* kbase = k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row;
     const uint16_t* vbase = v_cache + (int64_t)g * D;
 
-    // Loads block min(j, nblk-1): always issued, so the wait counts stay exact.
-    // Unless blocks are shared between rows, V goes through nontemporal
-    // (streaming) loads: each V load covers whole rows and is read once, and
-    // measured faster that way. K keeps plain loads: two of its loads cover
-    // the two halves of one 128-byte line, which streaming loads re-fetch.
-    auto load_block = [&](int j, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
-      const int jj = min(j, nblk - 1);
-      const int64_t blk = __builtin_amdgcn_readlane(my_blk, jj);
+    // Loads the wave's block min(k, nmine-1): always issued, so the wait
+    // counts stay exact. Unless blocks are shared between rows, V goes
+    // through nontemporal (streaming) loads: each V load covers whole rows
+    // and is read once, and measured faster that way. K keeps plain loads:
+    // two of its loads cover the two halves of one 128-byte line, which
+    // streaming loads re-fetch.
+    auto load_block = [&](int k, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
+      const int64_t blk = __builtin_amdgcn_readlane(my_blk, min(k, nmine - 1));
       const int64_t boff = blk * kBlock * kv_row;
       const u32x4* kp = (const u32x4*)(kbase + boff);
 #pragma unroll
@@ -191,9 +169,9 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
       }
     };
 
-    auto process_block = [&](int j, const u32x4 (&kk)[Sh::kKChunks],
+    auto process_block = [&](int k, const u32x4 (&kk)[Sh::kKChunks],
                              const u32x4 (&vv)[Sh::kVChunks]) {
-      const int tokb = (b_begin + j) * kBlock;
+      const int tokb = (b_begin + w + k * W) * kBlock;
       // V block into this wave's LDS slice, rows past the sequence zeroed.
 #pragma unroll
       for (int c = 0; c < Sh::kVChunks; ++c) {
@@ -246,82 +224,79 @@ __global__ __launch_bounds__(kMaxWavesPerGroup * kWave) void decode_partition_ke
       wave_lds_fence();
     };
 
+    // The main loop runs whole rounds of NBUF blocks with no early exit, so
+    // the loads still in flight at its back-edge are always the same NBUF-1
+    // ring slots in the same order and every wait is for exactly the block
+    // being consumed (an exit inside the round makes the wait at the loop
+    // head drain all loads). Block k0 + v of the last partial round already
+    // sits in slot v.
     u32x4 kb[NBUF][Sh::kKChunks], vb[NBUF][Sh::kVChunks];
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u) load_block(u, kb[u], vb[u]);
-    for (int j0 = 0; j0 < nblk; j0 += NBUF) {
+    int k0 = 0;
+    for (; k0 + NBUF <= nmine; k0 += NBUF) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
-        const int j = j0 + u;
-        if (j >= nblk) break;
-        load_block(j + NBUF - 1, kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF]);
-        process_block(j, kb[u], vb[u]);
+        load_block(k0 + u + NBUF - 1, kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF]);
+        process_block(k0 + u, kb[u], vb[u]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (k0 + u < nmine) process_block(k0 + u, kb[u], vb[u]);
     lsum = sum_across_groups(lsum);
   }
 
-  if (nparts == 1) {
-    if (!active || hl >= G) return;
-    const float inv = 1.0f / lsum;
-    uint16_t* op = out + ((int64_t)t0 * Hq + qh) * D + 4 * grp;
+  // Merge the W waves' states through LDS (the V slices are free once every
+  // wave has passed the barrier), kMergeHeads heads per pass:
+  //   M = max_w m_w, l = sum_w 2^(m_w - M) l_w, o = sum_w 2^(m_w - M) o_w,
+  // in wave order (deterministic). A wave without blocks holds m = -inf,
+  // l = 0, o = 0 and adds nothing; wave 0 always has a block.
+  float* mo = (float*)lds;                                       // [W][8][D + 4]
+  float* mml = mo + (size_t)W * Sh::kMergeHeads * Sh::kMergeRow;  // [W][8][2]
+  for (int hb = 0; hb < G; hb += Sh::kMergeHeads) {
+    __syncthreads();
+    const int hh = hl - hb;
+    if (hl < G && hh >= 0 && hh < Sh::kMergeHeads) {
+      float* orow = mo + (w * Sh::kMergeHeads + hh) * Sh::kMergeRow + 4 * grp;
 #pragma unroll
-    for (int mi = 0; mi < Sh::kDTiles; ++mi) {
-      u32x2 pr = {pack_bf16x2(o[mi][0] * inv, o[mi][1] * inv),
-                  pack_bf16x2(o[mi][2] * inv, o[mi][3] * inv)};
-      *(u32x2*)(op + 16 * mi) = pr;
-    }
-    return;
-  }
-  if (active && hl < G) {
-    const int64_t base = ((int64_t)s * num_parts_max + part) * Hq + qh;
-    float* wo = ws_o + base * D + 4 * grp;
-    if (fused) {  // read by another workgroup of this kernel, maybe on another XCD
-#pragma unroll
-      for (int mi = 0; mi < Sh::kDTiles; ++mi)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) store_coherent(wo + 16 * mi + e, o[mi][e]);
+      for (int mi = 0; mi < Sh::kDTiles; ++mi) *(f32x4*)(orow + 16 * mi) = o[mi];
       if (grp == 0) {
-        store_coherent(ws_ml + base * 2 + 0, m);
-        store_coherent(ws_ml + base * 2 + 1, lsum);
-      }
-    } else {  // read by the combine kernel after this one ends
-#pragma unroll
-      for (int mi = 0; mi < Sh::kDTiles; ++mi) *(f32x4*)(wo + 16 * mi) = o[mi];
-      if (grp == 0) {
-        ws_ml[base * 2 + 0] = m;
-        ws_ml[base * 2 + 1] = lsum;
+        mml[(w * Sh::kMergeHeads + hh) * 2 + 0] = m;
+        mml[(w * Sh::kMergeHeads + hh) * 2 + 1] = lsum;
       }
     }
-  }
-  if (!fused) return;
-
-  // Last-arriving workgroup of this (row, head group) merges the partitions.
-  // The partials went out as coherent stores; waiting for them to complete
-  // before the barrier orders them before the arrival count, and the merge
-  // reads them with coherent loads.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int32_t* ctr = counters + (int64_t)s * gridDim.z + blockIdx.z;
-  if (threadIdx.x == 0)
-    last_flag = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                nparts - 1;
-  __syncthreads();
-  if (!last_flag) return;
-  if (threadIdx.x == 0)  // ready for the next call
-    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!active) return;
-  const int64_t row0 = (int64_t)s * num_parts_max * Hq;  // + p*Hq + head
-  for (int idx = lane; idx < G * (D / 4); idx += kWave) {
-    const int h = idx / (D / 4);
-    const int head = g * G + h;
-    merge_head_quad<D>(ws_o, ws_ml, out, row0 + head, Hq, nparts,
-                       ((int64_t)t0 * Hq + head) * D, idx % (D / 4));
+    __syncthreads();
+    const int nh = min(Sh::kMergeHeads, G - hb);
+    for (int idx = threadIdx.x; idx < nh * (D / 2); idx += blockDim.x) {
+      const int h = idx / (D / 2);
+      const int d = 2 * (idx % (D / 2));
+      float M = -INFINITY;
+      for (int v = 0; v < W; ++v) M = fmaxf(M, mml[(v * Sh::kMergeHeads + h) * 2]);
+      float den = 0.f, n0 = 0.f, n1 = 0.f;
+      for (int v = 0; v < W; ++v) {
+        const float* ml = mml + (v * Sh::kMergeHeads + h) * 2;
+        const float e = fast_exp2(ml[0] - M);
+        const float* orow = mo + (v * Sh::kMergeHeads + h) * Sh::kMergeRow + d;
+        den += e * ml[1];
+        n0 += e * orow[0];
+        n1 += e * orow[1];
+      }
+      const int head = g * G + hb + h;
+      if (nparts == 1) {
+        const float inv = 1.0f / den;
+        *(uint32_t*)(out + ((int64_t)t0 * Hq + head) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+      } else {  // read by the combine kernel after this one ends
+        const int64_t base = ((int64_t)s * num_parts_max + part) * Hq + head;
+        *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
+        if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
+      }
+    }
   }
 }
 
-// Separate merge for rows with many partitions: one wave per (row, head),
-// lanes across d, partitions in order (deterministic).
+// Merge of a row's partitions: one wave per (row, head), lanes across d,
+// partitions in order (deterministic). Rows vary fastest in the grid.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
@@ -329,8 +304,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     int32_t Hq, int32_t part_tokens, int32_t num_parts_max) {
   constexpr int kPer = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int s = blockIdx.y;
-  const int qh = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int s = blockIdx.x;
+  const int qh = blockIdx.y * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (qh >= Hq) return;
   const int t0 = qsl[s];
   if (qsl[s + 1] - t0 != 1) return;
@@ -388,22 +363,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 
 template <int D, int NBUF, bool kStreamV>
 hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
-  const int waves = a.num_kv_heads < kMaxWavesPerGroup ? a.num_kv_heads : kMaxWavesPerGroup;
-  const int groups = (a.num_kv_heads + waves - 1) / waves;
+  using Sh = DecodeShape<D>;
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  dim3 grid(p.num_parts_max, a.num_seqs, groups);
+  dim3 grid(a.num_seqs, a.num_kv_heads, p.num_parts_max);
+  const size_t lds = (size_t)p.waves * Sh::kLdsWave * sizeof(uint16_t);
   profile_begin(PA_KERNEL_DECODE, stream);
-  hipLaunchKernelGGL((decode_partition_kernel<D, NBUF, kStreamV>), grid, dim3(waves * kWave), 0,
+  hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV>), grid, dim3(p.waves * kWave), lds,
                      stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                      (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
-                     (uint16_t*)a.out, p.ws_o, p.ws_ml, p.counters, scale_log2, a.num_q_heads,
+                     (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                      a.num_kv_heads, a.num_q_heads / a.num_kv_heads, a.max_blocks_per_seq,
-                     p.part_tokens, p.num_parts_max, waves, p.fused ? 1 : 0);
+                     p.part_tokens, p.num_parts_max);
   profile_end(PA_KERNEL_DECODE, stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.fused || p.num_parts_max <= 1) return e;
-  dim3 cgrid((a.num_q_heads + 3) / 4, a.num_seqs);
+  if (e != hipSuccess || p.num_parts_max <= 1) return e;
+  dim3 cgrid(a.num_seqs, (a.num_q_heads + 3) / 4);
   profile_begin(PA_KERNEL_COMBINE, stream);
   hipLaunchKernelGGL(decode_combine_kernel<D>, cgrid, dim3(256), 0, stream, a.seq_lens,
                      a.query_start_loc, p.ws_o, p.ws_ml, (uint16_t*)a.out, a.num_q_heads,
@@ -414,27 +389,32 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
 
 }  // namespace
 
-int32_t decode_groups(int32_t num_kv_heads) {
-  const int waves = num_kv_heads < kMaxWavesPerGroup ? num_kv_heads : kMaxWavesPerGroup;
-  return (num_kv_heads + waves - 1) / waves;
+int32_t decode_max_waves(int32_t head_size, int32_t prefetch) {
+  switch (head_size) {
+    case 64: return prefetch >= 3 ? max_waves<64, 3>() : max_waves<64, 2>();
+    case 128: return max_waves<128, 2>();
+    default: return 0;
+  }
 }
 
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
-  if (p.part_tokens <= 0 || p.part_tokens % kBlock || p.part_tokens > kMaxPartTokens)
+  const int maxw = decode_max_waves(a.head_size, p.prefetch);
+  if (p.waves < 1 || p.waves > maxw || p.part_tokens <= 0 || p.part_tokens % kBlock ||
+      p.part_tokens / kBlock > kWave * p.waves || p.num_parts_max > 65535 ||
+      a.num_kv_heads > 65535)
     return hipErrorInvalidValue;
-  const int nbuf = p.prefetch;
+  // Ring depths that fit the register budget of kMaxWaves waves per CU
+  // without spills: 2 or 3 blocks at D = 64, 2 at D = 128.
   const bool sv = p.stream_v;
-#define PA_DECODE_CASE(DD)                                                            \
-  if (nbuf <= 2) return sv ? launch_decode_nb<DD, 2, true>(a, p, stream)             \
-                           : launch_decode_nb<DD, 2, false>(a, p, stream);           \
-  if (nbuf == 3) return sv ? launch_decode_nb<DD, 3, true>(a, p, stream)             \
-                           : launch_decode_nb<DD, 3, false>(a, p, stream);           \
-  return sv ? launch_decode_nb<DD, 4, true>(a, p, stream)                            \
-            : launch_decode_nb<DD, 4, false>(a, p, stream);
   switch (a.head_size) {
-    case 64: { PA_DECODE_CASE(64) }
-    case 128: { PA_DECODE_CASE(128) }
-#undef PA_DECODE_CASE
+    case 64:
+      if (p.prefetch >= 3) return sv ? launch_decode_nb<64, 3, true>(a, p, stream)
+                                     : launch_decode_nb<64, 3, false>(a, p, stream);
+      return sv ? launch_decode_nb<64, 2, true>(a, p, stream)
+                : launch_decode_nb<64, 2, false>(a, p, stream);
+    case 128:
+      return sv ? launch_decode_nb<128, 2, true>(a, p, stream)
+                : launch_decode_nb<128, 2, false>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

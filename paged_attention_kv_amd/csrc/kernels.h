@@ -32,20 +32,21 @@ struct ForwardArgs {
   int32_t max_query_len, max_seq_len;  // resolved upper bounds (hints or defaults)
 };
 
-// Decode rows (q_len == 1): split-K partials or direct output, then combine.
+// Decode rows (q_len == 1): one workgroup per (row, KV head, partition);
+// direct output for rows of one partition, else partials and a combine.
 struct DecodePlan {
-  int32_t part_tokens;    // tokens per split-K partition (multiple of 16)
-  int32_t num_parts_max;  // partitions per row (grid x; workspace stride)
-  int32_t prefetch;       // register ring depth in 16-token blocks (2..4)
-  bool fused;             // last-arriving workgroup merges (else a combine kernel)
+  int32_t part_tokens;    // tokens per partition (multiple of 16, <= 1024 * waves)
+  int32_t num_parts_max;  // partitions per row (grid z, <= 65535; workspace stride)
+  int32_t waves;          // waves per workgroup (1..decode_max_waves)
+  int32_t prefetch;       // register ring depth in 16-token blocks (2, or 3 at D = 64)
   bool stream_v;          // V through nontemporal loads (blocks not shared)
   float* ws_o;            // [S][num_parts_max][Hq][D] unnormalised partial outputs
   float* ws_ml;           // [S][num_parts_max][Hq][2] reference max (log2 units) and sum
-  int32_t* counters;      // [S][decode_groups(Hkv)] arrival counters, zero between calls
 };
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream);
-// Workgroups along the KV-head axis of the decode grid.
-int32_t decode_groups(int32_t num_kv_heads);
+// Most waves a decode workgroup may hold for this head size and ring depth
+// (0: head size not built).
+int32_t decode_max_waves(int32_t head_size, int32_t prefetch);
 
 // Prefill rows (q_len > 1): a planner writes the tile list, then the tiles run.
 struct PrefillPlan {
@@ -65,7 +66,7 @@ int32_t prefill_split_tiles_per_row(int32_t group);
 // Workspace layout shared by pa_forward and pa_forward_workspace_bytes.
 struct WorkspaceLayout {
   int32_t part_tokens, num_parts_max, tile_queries, bound_a, bound_b;
-  size_t off_ctr, off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
+  size_t off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
 };
 bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,

@@ -35,12 +35,12 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 constexpr int32_t kMinPartTokens = 128;
-constexpr int32_t kMaxPartTokens = 1024;
+// Longest decode partition when rows are split for balance: a single
+// workgroup streaming a much longer row would outlast the rest of the grid.
+constexpr int32_t kBalancePartTokens = 4096;
+constexpr int32_t kComputeUnits = 256;  // MI355X
 constexpr size_t kAlign = 256;
-// Split-K arrival counters sit in a region of fixed size at the start of
-// every workspace, so no call of any shape ever writes data over the
-// counters another call relies on being zero.
-constexpr int64_t kCounterSlots = 1 << 16;
+constexpr int64_t kMaxGridZ = 65535;  // partitions per row ride on grid z
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -56,21 +56,37 @@ int32_t resolved_max_seq_len(int32_t max_blocks_per_seq, int32_t hint) {
   return hint > 0 ? std::min(hint, cap) : cap;
 }
 
-// Tokens per split-K partition of a decode row: the largest size that still
-// yields at least one workgroup per CU of a 256-CU part when every row is as
-// long as the longest. PA_DECODE_PART_TOKENS overrides it (multiple of 16 in
-// [128, 1024]) for tuning sweeps.
-int32_t choose_part_tokens(int32_t num_seqs, int32_t max_len) {
+// Waves per decode workgroup (they take a partition's blocks in turn). Four
+// measured best on every decode workload tried (2..16 swept): more waves
+// per CU add outstanding misses without adding bandwidth. PA_DECODE_WAVES
+// overrides it for tuning sweeps, up to what fits on a CU.
+constexpr int32_t kDecodeWaves = 4;
+int32_t decode_waves(int32_t head_size, int32_t prefetch) {
+  static const int v = env_int("PA_DECODE_WAVES", 1, 16, 0);
+  const int32_t maxw = std::max(1, pa::decode_max_waves(head_size, prefetch));
+  return std::min(v > 0 ? v : kDecodeWaves, maxw);
+}
+
+// Tokens per partition of a decode row. When rows x KV heads already give
+// every CU a workgroup, rows stay whole up to kBalancePartTokens (rows of one
+// partition skip the combine pass); otherwise rows are split until the
+// workgroups cover all CUs. A partition holds at most 64 blocks per wave.
+// PA_DECODE_PART_TOKENS overrides it (a multiple of 16) for tuning sweeps.
+int32_t choose_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t waves,
+                           int32_t max_len) {
+  const int32_t cap = 64 * waves * PA_BLOCK_SIZE;
   static const int32_t env = [] {
-    const int v = env_int("PA_DECODE_PART_TOKENS", kMinPartTokens, kMaxPartTokens, 0);
+    const int v = env_int("PA_DECODE_PART_TOKENS", kMinPartTokens, 1 << 20, 0);
     return v % PA_BLOCK_SIZE == 0 ? v : 0;
   }();
-  if (env) return env;
-  for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
-    const int64_t items = (int64_t)num_seqs * ((max_len + p - 1) / p);
-    if (items >= 256) return p;
-  }
-  return kMinPartTokens;
+  if (env) return std::min(env, cap);
+  const int64_t items = std::max<int64_t>(1, (int64_t)num_seqs * num_kv_heads);
+  int64_t nparts = items >= kComputeUnits ? 1 : (kComputeUnits + items - 1) / items;
+  nparts = std::max<int64_t>(nparts, (max_len + kBalancePartTokens - 1) / kBalancePartTokens);
+  nparts = std::max<int64_t>(nparts, (max_len + cap - 1) / cap);
+  int64_t part = (max_len + nparts - 1) / nparts;
+  part = (part + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE * PA_BLOCK_SIZE;
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(part, kMinPartTokens), cap);
 }
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
@@ -78,17 +94,9 @@ bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 ||
 // Register ring depth of the decode kernel (blocks in flight per wave);
 // PA_DECODE_PREFETCH overrides it for tuning sweeps.
 int32_t decode_prefetch(int32_t head_size) {
-  static const int v = env_int("PA_DECODE_PREFETCH", 2, 4, 0);
-  return v ? v : (head_size <= 64 ? 3 : 2);
-}
-
-// Rows with at most this many partitions are merged by their last-arriving
-// workgroup, the others by the separate combine kernel. PA_DECODE_FUSED_MAX
-// sets it (0..16); the default 0 always uses the combine kernel, which
-// measured faster on every workload tried.
-int32_t fused_max_parts() {
-  static const int v = env_int("PA_DECODE_FUSED_MAX", 0, 16, 0);
-  return v;
+  static const int v = env_int("PA_DECODE_PREFETCH", 2, 3, 0);
+  if (head_size > 64) return 2;
+  return v ? v : 2;
 }
 
 }  // namespace
@@ -105,9 +113,11 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   if (!supported_group(group)) return false;
   const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
   WorkspaceLayout w;
-  w.part_tokens = choose_part_tokens(num_seqs, max_len);
+  w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads,
+                                     decode_waves(head_size, decode_prefetch(head_size)), max_len);
   // Reserve for the smallest partition size so any tuning choice fits.
   w.num_parts_max = (max_len + kMinPartTokens - 1) / kMinPartTokens;
+  if (w.num_parts_max > kMaxGridZ) return false;
   w.tile_queries = prefill_tile_queries(group);
   // Each row adds at most one partial tile: sum ceil(ql/BQ) <= T/BQ + S.
   const int64_t any_bound = (int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
@@ -115,8 +125,7 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   w.bound_b = (int32_t)std::min<int64_t>(
       any_bound, (int64_t)num_seqs * prefill_split_tiles_per_row(group));
   const size_t rows = (size_t)num_seqs * w.num_parts_max * num_q_heads;
-  w.off_ctr = 0;
-  w.off_o = round_up((size_t)kCounterSlots * sizeof(int32_t), kAlign);
+  w.off_o = 0;
   w.off_ml = round_up(w.off_o + rows * head_size * sizeof(float), kAlign);
   w.off_counts = round_up(w.off_ml + rows * 2 * sizeof(float), kAlign);
   w.off_tiles_a = w.off_counts + kAlign;
@@ -270,12 +279,10 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
   dp.part_tokens = w.part_tokens;
   dp.num_parts_max = (a.max_seq_len + w.part_tokens - 1) / w.part_tokens;
   dp.prefetch = decode_prefetch(head_size);
+  dp.waves = decode_waves(head_size, dp.prefetch);
   dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
-  dp.fused = dp.num_parts_max > 1 && dp.num_parts_max <= fused_max_parts() &&
-             (int64_t)num_seqs * pa::decode_groups(num_kv_heads) <= kCounterSlots;
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
-  dp.counters = (int32_t*)(ws + w.off_ctr);
   hipError_t e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward decode launch");
   return PA_OK;

@@ -194,14 +194,18 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
 #pragma unroll
     for (int mi = 0; mi < DT; ++mi) o[mt][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {-INFINITY, -INFINITY};  // reference max per row, log2 units
-  float lsum[2] = {0.f, 0.f};
+  // Row sums of the weights, accumulated by the matrix core as ones . P^T
+  // from the same bf16 P that multiplies V: every element of lsum[mt] holds
+  // the running sum of row hl.
+  f32x4 lsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
   const int32_t* table = block_table + (int64_t)s * MB;
   const int last_blk = (kv_end - 1) / kBlock;  // last block any row reads
   constexpr int kTileBlocks = BN / kBlock;     // 16-token blocks per key tile
   // Block ids of key tile kt: lane b < kTileBlocks holds entry kt*4 + b
   // (clamped to the last block read), fetched one iteration ahead.
-  auto tile_ids = [&](int kt) {
+  auto tile_ids = [&](int kt) __attribute__((always_inline)) {
     return lane < kTileBlocks ? table[min(kt * kTileBlocks + lane, last_blk)] : 0;
   };
   // Tile kt straight from HBM/L2 into LDS stage `stage`: load op j of wave w
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   // i.e. row r, physical chunk pc; it fetches logical chunk pc ^ swz(r) of
   // key kt*64 + r. The rows of one op lie in one 16-key block (wave-uniform
   // table id).
-  auto dma_tile = [&](int kt, int stage, int ids) {
+  auto dma_tile = [&](int kt, int stage, int ids) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const int p = (j * 4 + w) * 1024 + lane * 16;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   // Rows of tile kt at or past kv_end came from a clamped or partly used
   // block: zero their V (each thread the bytes it loaded itself, after its
   // own loads completed), so a zero weight never meets a stale value.
-  auto zero_tail = [&](int kt, int stage) {
+  auto zero_tail = [&](int kt, int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const int p = (j * 4 + w) * 1024 + lane * 16;
@@ -236,9 +240,26 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
     }
   };
 
+  // Per-lane LDS byte offsets of the operand reads, so that the rest of each
+  // address is a compile-time immediate.
+  // K (QK A operand): lane reads row n*16 + hl, logical chunk 4i + grp, which
+  // sits at chunk (4i + grp) ^ swz_k(hl) = 8*(i/2) + ((4*(i%2) + grp) ^ (hl%8)).
+  int koff[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) koff[b] = hl * RB + (((4 * b + grp) ^ swz_k(hl)) * 16);
+  // V (PV A operand, transpose reads): lane reads row kp*32 + 4*grp + hl/4
+  // (and 16 rows on), 8 bytes at half (hl%2) of logical chunk 2*mi + (hl%4)/2,
+  // which sits at chunk 8*(mi/4) + ((2*(mi%4) + (hl%4)/2) ^ swz_v(hl/4)).
+  int voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    voff[j] = (4 * grp + hl / 4) * RB + (hl & 1) * 8 +
+              (((2 * j + (hl % 4) / 2) ^ swz_v(hl / 4)) * 16);
+
   // One 64-key tile: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
   // split: P enters PV as bf16 hi + lo parts (rows with few visible keys).
-  auto compute_tile = [&](int kt, int stage, bool masked, auto split_tag) {
+  auto compute_tile = [&](int kt, int stage, bool masked, auto split_tag)
+      __attribute__((always_inline)) {
     constexpr bool kSplit = decltype(split_tag)::value;
     const uint8_t* kst = ks[stage];
     const uint8_t* vst = vs[stage];
@@ -251,8 +272,7 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
     for (int n = 0; n < NS; ++n) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
-        const int r = n * 16 + hl;
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + r * RB + ((4 * i + grp) ^ swz_k(r)) * 16));
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + n * 16 * RB + koff[i & 1] + (i >> 1) * 128));
         st[0][n] = mfma_16x16x32(a, qv[0][i], st[0][n]);
         st[1][n] = mfma_16x16x32(a, qv[1][i], st[1][n]);
       }
@@ -270,14 +290,19 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
     }
     // Lazy reference max (log2 units): re-reference a row only when one of
     // its scores exceeds the current reference by more than 2^kLazyP.
+    // NaN-propagating maximum (masked scores are already -inf): needs no
+    // canonicalisation of the MFMA results and maps to 3-input maxima.
     float lmax[2];
     bool over = false;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      float v = -INFINITY;
+      float va = st[mt][0][0], vb = st[mt][0][1];
 #pragma unroll
-      for (int n = 0; n < NS; ++n)
-        v = fmaxf(v, fmaxf(fmaxf(st[mt][n][0], st[mt][n][1]), fmaxf(st[mt][n][2], st[mt][n][3])));
+      for (int i = 2; i < 4 * NS; i += 2) {
+        va = __builtin_elementwise_maximum(va, st[mt][i / 4][i % 4]);
+        vb = __builtin_elementwise_maximum(vb, st[mt][i / 4][i % 4 + 1]);
+      }
+      const float v = __builtin_elementwise_maximum(va, vb);
       lmax[mt] = v * scale_log2;
       over |= lmax[mt] > m[mt] + kLazyP;
     }
@@ -295,16 +320,11 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const float negm = -m[mt];
-      float ps = 0.f;
 #pragma unroll
       for (int n = 0; n < NS; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[mt][n][r], scale_log2, negm));
-          st[mt][n][r] = p;
-          ps += p;
-        }
-      lsum[mt] += ps;
+        for (int r = 0; r < 4; ++r)
+          st[mt][n][r] = fast_exp2(__builtin_fmaf(st[mt][n][r], scale_log2, negm));
     }
     // O^T += V^T P^T per 32-key pair; the A operand holds keys
     // {4*grp+r, 16+4*grp+r} of the pair for d = 16*mi + hl (two transpose
@@ -333,14 +353,12 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
           pb[mt] = as_bf16x8(hv);
         }
       }
-      const int r0 = kp * 32 + 4 * grp + hl / 4;  // rows r0 and r0 + 16 share swz_v
-      const uint8_t* vrow0 = vst + r0 * RB + ((hl % 4) & 1) * 8;
-      const uint8_t* vrow1 = vrow0 + 16 * RB;
+      const uint8_t* vrow0 = vst + kp * 32 * RB;
 #pragma unroll
       for (int mi = 0; mi < DT; ++mi) {
-        const int c = (2 * mi + (hl % 4) / 2) ^ swz_v(r0);
-        const i16x4 a0 = lds_read_tr16((const uint16_t*)(vrow0 + c * 16));
-        const i16x4 a1 = lds_read_tr16((const uint16_t*)(vrow1 + c * 16));
+        const uint8_t* va = vrow0 + voff[mi & 3] + (mi >> 2) * 128;
+        const i16x4 a0 = lds_read_tr16((const uint16_t*)va);
+        const i16x4 a1 = lds_read_tr16((const uint16_t*)(va + 16 * RB));
         const bf16x8 av = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         o[0][mi] = mfma_16x16x32(av, pb[0], o[0][mi]);
@@ -350,35 +368,43 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
           o[1][mi] = mfma_16x16x32(av, pl[1], o[1][mi]);
         }
       }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        lsum[mt] = mfma_16x16x32(ones, pb[mt], lsum[mt]);
+        if constexpr (kSplit) lsum[mt] = mfma_16x16x32(ones, pl[mt], lsum[mt]);
+      }
     }
   };
 
 
-  dma_tile(0, 0, tile_ids(0));
+  // One key tile; the loop is unrolled by two so that the LDS stage of each
+  // half is a compile-time constant (LDS offsets become immediates).
   int ids_next = tile_ids(1);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // This wave's loads into stage kt%2 are complete (the barrier's release
+  auto step = [&](int kt, int stage) __attribute__((always_inline)) {
+    // This wave's loads into `stage` are complete (the barrier's release
     // waits for all of them), every wave's are once all have arrived, and
-    // every wave is done reading tile kt-1 from stage (kt+1)%2.
+    // every wave is done reading tile kt-1 from the other stage.
     __syncthreads();
     if ((kt + 1) * BN > kv_end) {
-      zero_tail(kt, kt & 1);
+      zero_tail(kt, stage);
       __syncthreads();
     }
     if (kt + 1 < ntiles) {
-      dma_tile(kt + 1, (kt + 1) & 1, ids_next);
+      dma_tile(kt + 1, stage ^ 1, ids_next);
       ids_next = tile_ids(kt + 2);
     }
     const bool masked = (kt + 1) * BN - 1 > first_lim;
     // Tiles whose rows see at most kSplitKeys keys (SPLIT) keep P to about
     // 2^-17 (hi + lo): few weights carry each output there, and bf16
     // rounding of P would show in it.
-    compute_tile(kt, kt & 1, masked, std::integral_constant<bool, SPLIT>{});
-  }
+    compute_tile(kt, stage, masked, std::integral_constant<bool, SPLIT>{});
+  };
+  dma_tile(0, 0, tile_ids(0));
+  for (int kt = 0; kt < ntiles; ++kt) step(kt, kt & 1);
 
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const float ltot = sum_across_groups(lsum[mt]);
+    const float ltot = lsum[mt][0];
     const int row = w * 32 + mt * 16 + hl;
     const int tl = row / G;
     const int hh = row % G;
@@ -422,6 +448,7 @@ hipError_t launch_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t 
   const float scale_log2 = a.scale * 1.4426950408889634f;
   if (p.bound_a > 0) {
     const int64_t grid = ((int64_t)p.bound_a * a.num_kv_heads + 7) / 8 * 8;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
     profile_begin(PA_KERNEL_PREFILL, stream);
     hipLaunchKernelGGL((prefill_tile_kernel<D, G, false>), dim3((unsigned)grid),
                        dim3(kPrefillThreads), 0, stream, (const uint16_t*)a.q,

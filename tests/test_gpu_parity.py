@@ -305,16 +305,20 @@ def test_validate_inputs_accepts_good_and_names_bad_metadata():
 
 
 def test_workspace_shared_by_calls_of_different_shapes():
-    """One cached workspace serves calls whose split-K layouts differ: a call
-    merged by its last workgroup, one merged by the combine kernel (many
-    partitions, fewer rows), then the first shape again. Regression test for
-    arrival counters that a later call's partials overwrote."""
-    fused = wl.custom("ws_fused", 32, 8, 128, rows=[(1, 4000)] * 40, seed=47)
+    """One workspace, filled with 0xFF bytes (NaN as fp32) before the first
+    call, serves calls whose split-K layouts differ: few partitions and many
+    rows, then many partitions and few rows, alternately. Every call must
+    write what it reads (the workspace may hold anything between calls)."""
+    few = wl.custom("ws_few", 32, 8, 128, rows=[(1, 4000)] * 40, seed=47)
     many = wl.custom("ws_many", 64, 8, 128, rows=[(1, 30000), (1, 20000)], seed=48)
-    for spec in (fused, many, fused, many, fused):
+    nbytes = max(pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads,
+                                            s.num_kv_heads, s.head_size, s.max_blocks_per_seq)
+                 for s in (few, many))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    for spec in (few, many, few, many, few):
         banner(f"workspace reuse: {spec.name}")
         case = wl.make_case(spec, device=DEV)
-        out = write_and_forward(case)
+        out = write_and_forward(case, workspace=ws)
         pick = list(range(0, spec.num_seqs, max(1, spec.num_seqs // 6)))
         r, want = oracle_rows(case, pick)
         assert_close(out.cpu()[r], want, spec.name)
