@@ -86,12 +86,16 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                    int64_t num_blocks, int32_t block_size, void* stream);
 
 /*
- * Workspace bytes pa_forward needs for these sizes: the split-K partial
- * results of decode rows and the work list of prefill tiles. Depends only on
- * its arguments; returns 0 if an argument is out of range or the sizes are
- * not supported (more than 65535 split-K partitions of 128 tokens per row).
+ * Workspace bytes pa_forward needs for these sizes: a fixed region of
+ * PA_WORKSPACE_COUNTER_BYTES at the start holding per-row arrival counters
+ * of the decode rows (zero before the first call, left zero by every call,
+ * never written with anything else), then partial results of decode rows
+ * split between workgroups and the work list of prefill tiles. Depends only
+ * on its arguments (and on the tuning overrides read once per process);
+ * returns 0 if an argument is out of range or the sizes are not supported.
  * max_seq_len_hint <= 0 means "unknown" (max_blocks_per_seq * 16 is used).
  */
+#define PA_WORKSPACE_COUNTER_BYTES (256u * 1024u)
 size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_size,
                                   int32_t max_blocks_per_seq, int32_t max_seq_len_hint);
@@ -116,21 +120,27 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  *                    are used). A hint below the true maximum is a contract
  *                    violation (rows past it are not computed).
  *   workspace        device, >= pa_forward_workspace_bytes(...) bytes,
- *                    16-byte aligned, any contents: scratch that each call
- *                    writes before it reads. Calls that share a workspace
- *                    must be ordered on one stream.
+ *                    16-byte aligned. Its first PA_WORKSPACE_COUNTER_BYTES
+ *                    must be zero before its first use (every call leaves
+ *                    them zero); the rest is scratch that each call writes
+ *                    before it reads. Calls that share a workspace must be
+ *                    ordered on one stream.
  *
  * Query row i of sequence s (i < q_len = qsl[s+1] - qsl[s]) sits at position
  * c + i with c = seq_lens[s] - q_len and attends to keys 0..c+i of its own
  * sequence; query head h reads KV head h / (num_q_heads / num_kv_heads).
  * Rows with q_len == 0 produce nothing; rows with q_len == 1 take the decode
- * path (split-K over the context), rows with q_len > 1 the prefill path.
+ * path (for large batches the rows' blocks are shared out evenly between
+ * workgroups; small batches, or more than 4096 rows, split rows into fixed
+ * partitions), rows with q_len > 1 the prefill path.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
  * Tuning overrides, read once per process (for sweeps; out-of-range values
- * are ignored): PA_DECODE_PART_TOKENS (tokens per decode partition, a
- * multiple of 16, at least 128), PA_DECODE_WAVES (waves per decode
- * workgroup, 1..16 within the head size's limit), PA_DECODE_PREFETCH (blocks
- * in flight per wave at head_size 64, 2..3).
+ * are ignored): PA_DECODE_STREAM (0 / 1 = always the partitioned / the
+ * even-share decode schedule where it fits), PA_DECODE_STREAM_WGS
+ * (even-share workgroups, 1..512), PA_DECODE_PART_TOKENS (tokens per decode
+ * partition, a multiple of 16, at least 128), PA_DECODE_WAVES (waves per
+ * partitioned decode workgroup, 1..16 within the head size's limit),
+ * PA_DECODE_PREFETCH (blocks in flight per wave at head_size 64, 2..3).
  * Requires block_size == 16, head_size in {64, 128}, num_q_heads /
  * num_kv_heads in {1, 2, 4, 8, 16}. Caller contract: 0 <= q_len <= seq_len
  * <= max_blocks_per_seq * 16 and the first ceil(seq_len / 16) table entries

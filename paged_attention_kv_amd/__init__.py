@@ -22,6 +22,7 @@ __all__ = ["cache_write", "forward", "forward_workspace_bytes", "validate_inputs
 
 BLOCK_SIZE = 16
 FORWARD_SHARED_BLOCKS = 1  # PA_FORWARD_SHARED_BLOCKS
+WORKSPACE_COUNTER_BYTES = 256 * 1024  # PA_WORKSPACE_COUNTER_BYTES
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
 _lib = None
@@ -162,7 +163,9 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        # zero-filled once: the leading counter region must start at zero
+        # (every call leaves it zero)
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -176,7 +179,8 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
     paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
     ``max_seq_len`` are optional host upper bounds that shrink the launch
-    grids; ``workspace`` (uint8, on the device, any contents) is taken from a
+    grids; ``workspace`` (uint8, on the device, its first
+    ``WORKSPACE_COUNTER_BYTES`` zero before its first use) is taken from a
     per-device cache when omitted. ``shared_blocks``
     tells the library that some blocks appear in several rows' tables
     (prefix caching); results are the same either way."""

@@ -1,6 +1,5 @@
 // Decode rows of the flattened batch (one query token per sequence): paged
-// attention over the sequence's whole context, optionally split over the
-// context into partitions whose partial softmax states are then merged.
+// attention over the sequence's whole context.
 //
 // What is computed follows the pages "Inside vLLM: Anatomy of a
 // High-Throughput LLM Inference System": section "Scheduler" (decode requests
@@ -8,11 +7,8 @@
 // bandwidth; blocks hold 16 tokens) and section "Run forward pass" (block
 // tables index the paged KV memory; each sequence sees only its own tokens).
 //
-// Work decomposition (gfx950): a workgroup is one (sequence, KV head,
-// partition of the context) and holds W waves that take the partition's
-// 16-token blocks in turn (wave w: blocks w, w+W, ...), so that one CU keeps
-// many blocks in flight even when a row is short. Each wave keeps the G query
-// heads of the KV head in MFMA operands:
+// Per wave (gfx950): a wave owns one KV head of one row and streams 16-token
+// blocks, keeping the G query heads of that KV head in MFMA operands:
 //   S^T[16 tokens x 16 heads] = K[16 x D] . Q^T[D x 16]   (16x16x32 bf16 MFMA,
 //                                                          K straight from HBM)
 //   O^T[D x 16 heads]       += V^T[D x 16] . P^T[16 x 16] (16x16x16 bf16 MFMA,
@@ -21,22 +17,29 @@
 // the B operand layout of the second product, so P never leaves registers.
 // Blocks stream through a ring of NBUF register buffers whose loads are
 // issued unconditionally (indices clamped), so the compiler's wait counts
-// only ever wait for the block being consumed. At the end the W partial
-// softmax states are merged through LDS.
+// only ever wait for the block being consumed. Softmax: scores are kept in
+// log2 units against a per-head reference max m, re-referenced (one max
+// across the four 16-lane groups, accumulators rescaled) only when a score
+// exceeds it by more than 2^kLazy; weights stay <= 2^kLazy, which bf16 hi+lo
+// parts and fp32 accumulators carry without loss. Several waves of a
+// workgroup may hold partial states of one (row, KV head); they are merged
+// through LDS: M = max m_w, l = sum 2^(m_w - M) l_w, o = sum 2^(m_w - M) o_w,
+// in wave order.
 //
-// Softmax: scores are kept in log2 units against a per-head reference max m.
-// m is only recomputed (one max across the four 16-lane groups) and the
-// accumulators rescaled when some score exceeds m by more than 2^kLazy; in
-// between, weights are exp2(s - m) <= 2^kLazy, which bf16 hi+lo parts and the
-// fp32 accumulators carry without loss.
-//
-// Split-K: when rows x KV heads alone would leave CUs idle, rows are split
-// into partitions; a partition that is not its row's only one writes its
-// merged (m, l, o) to the workspace and a combine kernel merges the
-// partitions. (Merging in the last-arriving workgroup instead measured slower
-// on this chip: a row's partitions run on several XCDs, whose L2s are not
-// coherent with each other, so the hand-over costs three memory round trips
-// at the tail, more than the kernel boundary it saves.)
+// Two schedules:
+//  * stream (decode_stream_kernel): one persistent workgroup per CU takes an
+//    equal, contiguous share of all decode rows' blocks (rows in order, each
+//    row's blocks in order), with one wave per KV head (or several per head
+//    when there are few heads), so every CU streams the same number of bytes
+//    whatever the mix of lengths, and each block is read by all its heads at
+//    once. A row whose blocks fall into several shares is merged by the share
+//    that finishes last: the others publish their partial state with
+//    device-coherent stores and count themselves in on a per-row counter.
+//    (Row lengths are read on the device; the host never sees them.)
+//  * partitioned (decode_kernel): one workgroup per (row, KV head, fixed-size
+//    partition), W waves taking the partition's blocks in turn; rows of more
+//    than one partition are merged by decode_combine_kernel. Used when the
+//    batch has too many rows for the stream kernel's per-workgroup row scan.
 #include <math.h>
 
 #include "common.h"
@@ -57,11 +60,12 @@ struct DecodeShape {
   // banks apart so the four rows of one transpose read do not collide.
   static constexpr int kLdsRow = D + 16;
   static constexpr int kLdsWave = kBlock * kLdsRow;  // elements per wave
-  // Merge stage (fp32), heads handled per pass: o rows of D + 4 floats.
-  // W * 8 * (D + 4) * 4 + W * 8 * 8 bytes fit in the W V slices.
-  static constexpr int kMergeHeads = 8;
+  // Merge stage (fp32): kMergeCols query columns per pass, rows of D + 4
+  // floats; W * kMergeCols * (D + 4) * 4 + W * kMergeCols * 8 bytes fit in
+  // the W V slices.
+  static constexpr int kMergeCols = 8;
   static constexpr int kMergeRow = D + 4;
-  static_assert(kMergeHeads * (kMergeRow * 4 + 8) <= kLdsWave * 2, "merge stage fits in LDS");
+  static_assert(kMergeCols * (kMergeRow * 4 + 8) <= kLdsWave * 2, "merge stage fits in LDS");
 };
 
 // Most waves per decode workgroup: as many as fit on a CU at the kernel's
@@ -80,6 +84,424 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Device-coherent store and load of 8 bytes (agent scope, relaxed): they go
+// past this XCD's L2, so workgroups on different XCDs can hand data over.
+__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_coherent2(const float* p) {
+  const uint64_t v =
+      __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
+
+// Online-softmax state of one wave: O^T tiles (lane: d = 16*mi + 4*(l/16) + r,
+// query column l%16), the reference max and the running sum of weights.
+template <int D>
+struct WaveAcc {
+  f32x4 o[D / 16];
+  float m;
+  float lsum;
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int mi = 0; mi < D / 16; ++mi) o[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    lsum = 0.f;
+  }
+};
+
+// Q^T as the B operand: lane holds query column hl (< ncols, else zeros),
+// d = 32*i + 8*grp + e.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qv)[D / 32], const uint16_t* __restrict__ qrow,
+                                       int hl, int grp, int ncols) {
+  const u32x4* qp = (const u32x4*)(qrow + (int64_t)hl * D) + grp;
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qv[i] = as_bf16x8(hl < ncols ? qp[4 * i] : z);
+  }
+}
+
+// Streams nk (1..64) blocks of one KV head into acc: block k's id sits in lane
+// k of `ids`, its first token is tok0 + k * tok_step, and tokens >= tok_end
+// are masked (their V rows zeroed). kbase / vbase point at the head's slice
+// of block 0 (kbase already offset to the lane's K row and chunk); vl is the
+// wave's LDS slice.
+template <int D, int NBUF, bool kStreamV>
+__device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv)[D / 32], int ids,
+                                              int nk, int tok0, int tok_step, int tok_end,
+                                              const uint16_t* __restrict__ kbase,
+                                              const uint16_t* __restrict__ vbase, int64_t kv_row,
+                                              uint16_t* vl, float scale_log2, int lane) {
+  using Sh = DecodeShape<D>;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+
+  // Loads block min(k, nk-1): always issued, so the wait counts stay exact.
+  // Unless blocks are shared between rows, V goes through nontemporal
+  // (streaming) loads: each V load covers whole rows and is read once, and
+  // measured faster that way. K keeps plain loads: two of its loads cover the
+  // two halves of one 128-byte line, which streaming loads re-fetch.
+  auto load_block = [&](int k, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
+    const int64_t blk = __builtin_amdgcn_readlane(ids, min(k, nk - 1));
+    const int64_t boff = blk * kBlock * kv_row;
+    const u32x4* kp = (const u32x4*)(kbase + boff);
+#pragma unroll
+    for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = kp[4 * i];
+#pragma unroll
+    for (int c = 0; c < Sh::kVChunks; ++c) {
+      const int idx = c * kWave + lane;
+      const int row = idx / (D / 8);
+      const int col8 = idx % (D / 8);
+      const u32x4* vp = (const u32x4*)(vbase + boff + row * kv_row + col8 * 8);
+      vv[c] = kStreamV ? __builtin_nontemporal_load(vp) : *vp;
+    }
+  };
+
+  auto process_block = [&](int k, const u32x4 (&kk)[Sh::kKChunks],
+                           const u32x4 (&vv)[Sh::kVChunks]) {
+    const int tokb = tok0 + k * tok_step;
+    // V block into this wave's LDS slice, rows past the sequence zeroed.
+#pragma unroll
+    for (int c = 0; c < Sh::kVChunks; ++c) {
+      const int idx = c * kWave + lane;
+      const int row = idx / (D / 8);
+      const int col8 = idx % (D / 8);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *(u32x4*)(vl + row * Sh::kLdsRow + col8 * 8) = (tokb + row < tok_end) ? vv[c] : z;
+    }
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < Sh::kKChunks; ++i) sacc = mfma_16x16x32(as_bf16x8(kk[i]), qv[i], sacc);
+    float sv[4];
+    bool over = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tokb + 4 * grp + r;
+      sv[r] = tok < tok_end ? sacc[r] * scale_log2 : -INFINITY;
+      over |= sv[r] > acc.m + kLazy;
+    }
+    if (__any(over)) {  // wave-uniform: re-reference the softmax
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = max_across_groups(bm);
+      const float mn = fmaxf(acc.m, bm);
+      const float alpha = fast_exp2(acc.m - mn);
+      acc.lsum *= alpha;
+#pragma unroll
+      for (int mi = 0; mi < Sh::kDTiles; ++mi) acc.o[mi] *= alpha;
+      acc.m = mn;
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = fast_exp2(sv[r] - acc.m);
+      acc.lsum += p[r];
+    }
+    const u32x2 s01 = split_pack_bf16x2(p[0], p[1]);
+    const u32x2 s23 = split_pack_bf16x2(p[2], p[3]);
+    const i16x4 phi = __builtin_bit_cast(i16x4, u32x2{s01[0], s23[0]});
+    const i16x4 plo = __builtin_bit_cast(i16x4, u32x2{s01[1], s23[1]});
+    wave_lds_fence();
+    // A operand V^T[d = 16*mi + hl][token 4*grp + r] by transpose reads.
+    const uint16_t* vrow = vl + (4 * grp + hl / 4) * Sh::kLdsRow + 4 * (hl % 4);
+#pragma unroll
+    for (int mi = 0; mi < Sh::kDTiles; ++mi) {
+      const i16x4 a = lds_read_tr16(vrow + 16 * mi);
+      acc.o[mi] = mfma_16x16x16(a, phi, acc.o[mi]);
+      acc.o[mi] = mfma_16x16x16(a, plo, acc.o[mi]);
+    }
+    wave_lds_fence();
+  };
+
+  // The main loop runs whole rounds of NBUF blocks with no early exit, so
+  // the loads still in flight at its back-edge are always the same NBUF-1
+  // ring slots in the same order and every wait is for exactly the block
+  // being consumed (an exit inside the round makes the wait at the loop head
+  // drain all loads). Block k0 + v of the last partial round sits in slot v.
+  u32x4 kb[NBUF][Sh::kKChunks], vb[NBUF][Sh::kVChunks];
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) load_block(u, kb[u], vb[u]);
+  int k0 = 0;
+  for (; k0 + NBUF <= nk; k0 += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      load_block(k0 + u + NBUF - 1, kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF]);
+      process_block(k0 + u, kb[u], vb[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u)
+    if (k0 + u < nk) process_block(k0 + u, kb[u], vb[u]);
+}
+
+// Merges the states of waves that share a KV-head slot (slot = w % HG; waves
+// slot, slot + HG, ... of the W in the workgroup) through LDS, kMergeCols
+// query columns per pass, and calls out(slot, col, d, M, den, n0, n1) for
+// every column < ncols and even d: the merged state of d and d+1, summed in
+// wave order. A wave that streamed nothing holds m = -inf, l = 0, o = 0 and
+// adds nothing. Every wave of the workgroup must call it (it has barriers).
+template <int D, class Out>
+__device__ __forceinline__ void merge_waves(const WaveAcc<D>& acc, float* stage, int W, int HG,
+                                            int ncols, int w, int lane, Out&& out) {
+  using Sh = DecodeShape<D>;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int S = W / HG;
+  float* mo = stage;                                             // [W][8][D + 4]
+  float* mml = stage + (size_t)W * Sh::kMergeCols * Sh::kMergeRow;  // [W][8][2]
+  for (int cb = 0; cb < ncols; cb += Sh::kMergeCols) {
+    __syncthreads();  // the stage (or the V slices it overlays) is free
+    const int hh = hl - cb;
+    if (hl < ncols && hh >= 0 && hh < Sh::kMergeCols) {
+      float* orow = mo + (w * Sh::kMergeCols + hh) * Sh::kMergeRow + 4 * grp;
+#pragma unroll
+      for (int mi = 0; mi < Sh::kDTiles; ++mi) *(f32x4*)(orow + 16 * mi) = acc.o[mi];
+      if (grp == 0) {
+        mml[(w * Sh::kMergeCols + hh) * 2 + 0] = acc.m;
+        mml[(w * Sh::kMergeCols + hh) * 2 + 1] = acc.lsum;
+      }
+    }
+    __syncthreads();
+    const int nh = min(Sh::kMergeCols, ncols - cb);
+    const int per_slot = nh * (D / 2);
+    for (int idx = threadIdx.x; idx < HG * per_slot; idx += blockDim.x) {
+      const int slot = idx / per_slot;
+      const int h = (idx % per_slot) / (D / 2);
+      const int d = 2 * (idx % (D / 2));
+      float M = -INFINITY;
+      for (int sub = 0; sub < S; ++sub)
+        M = fmaxf(M, mml[((slot + HG * sub) * Sh::kMergeCols + h) * 2]);
+      float den = 0.f, n0 = 0.f, n1 = 0.f;
+      for (int sub = 0; sub < S; ++sub) {
+        const int v = slot + HG * sub;
+        const float* ml = mml + (v * Sh::kMergeCols + h) * 2;
+        const float e = fast_exp2(ml[0] - M);
+        const float* orow = mo + (v * Sh::kMergeCols + h) * Sh::kMergeRow + d;
+        den += e * ml[1];
+        n0 += e * orow[0];
+        n1 += e * orow[1];
+      }
+      out(slot, cb + h, d, M, den, n0, n1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stream schedule
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix sum over the workgroup (any blockDim <= 1024); `tmp`
+// holds 17 ints of LDS. Returns the thread's exclusive prefix; *total gets the
+// sum of all.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) tmp[w] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < nw; ++i) {
+      const int t = tmp[i];
+      tmp[i] = run;
+      run += t;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  const int r = tmp[w] + x - v;
+  *total = tmp[16];
+  __syncthreads();  // tmp may be reused
+  return r;
+}
+
+template <int D, int NBUF, bool kStreamV>
+__global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
+    uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+    int32_t* __restrict__ counters, float scale_log2, int32_t Hq, int32_t Hkv, int32_t G,
+    int32_t MB, int32_t S, int32_t HG) {
+  using Sh = DecodeShape<D>;
+  // LDS: W V slices (the merge stage overlays them), then the row prefix
+  // [S + 1], scan scratch [17] and a flag.
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int W = blockDim.x / kWave;
+  int32_t* pre = (int32_t*)(lds + (size_t)W * Sh::kLdsWave);
+  int32_t* tmp = pre + S + 1;
+  int32_t* flag = tmp + 17;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  // The wave index is uniform across the wave; saying so keeps the block
+  // loop and the table reads on scalar registers.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int Ssub = W / HG;
+  const int slot = w % HG;
+  const int sub = w / HG;
+  const int g = blockIdx.y * HG + slot;  // this wave's KV head
+  const bool head_ok = g < Hkv;
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t kv_row = (int64_t)Hkv * D;
+
+  // 1. Blocks per decode row (0 for other rows) and their exclusive prefix,
+  //    rows in order: thread t takes rows [t*R, t*R + R).
+  {
+    const int R = (S + blockDim.x - 1) / blockDim.x;
+    const int r_lo = min(S, (int)threadIdx.x * R);
+    const int r_hi = min(S, r_lo + R);
+    int mine = 0;
+    for (int s = r_lo; s < r_hi; ++s)
+      mine += (qsl[s + 1] - qsl[s] == 1) ? (seq_lens[s] + kBlock - 1) / kBlock : 0;
+    int total;
+    int run = block_exclusive_scan(mine, tmp, &total);
+    for (int s = r_lo; s < r_hi; ++s) {
+      pre[s] = run;
+      run += (qsl[s + 1] - qsl[s] == 1) ? (seq_lens[s] + kBlock - 1) / kBlock : 0;
+    }
+    if (threadIdx.x == 0) pre[S] = total;
+    __syncthreads();
+  }
+  const int64_t T = pre[S];
+  const int64_t P = min((int64_t)gridDim.x, T);  // every share holds >= 1 block
+  const int p = blockIdx.x;
+  if (p >= P) return;  // workgroup-uniform, after the last barrier of the scan
+  // Share p: blocks [B(p), B(p+1)) with B(c) = floor(c * T / P).
+  auto B = [&](int64_t c) { return c * T / P; };
+  const int64_t r0 = B(p), r1 = B(p + 1);
+  // First row: the last s with pre[s] <= r0 (rows of no blocks are skipped).
+  int s;
+  {
+    int lo = 0, hi = S;  // pre[lo] <= r0 < pre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) / 2;
+      if (pre[mid] <= r0) lo = mid; else hi = mid;
+    }
+    s = lo;
+  }
+
+  uint16_t* vl = lds + w * Sh::kLdsWave;
+  float* stage = (float*)lds;
+  WaveAcc<D> acc;
+  for (int64_t pos = r0; pos < r1; ++s) {
+    const int64_t a = pre[s], b = pre[s + 1];
+    if (b <= pos) continue;  // no blocks in this share (or none at all)
+    const int j_lo = (int)(pos - a);
+    const int j_hi = (int)(min(b, r1) - a);
+    pos = min(b, r1);
+    const int t0 = qsl[s];
+    const int L = seq_lens[s];
+    // Shares that hold blocks of this row: p_first .. p_last.
+    const int64_t p_first = ((a + 1) * P + T - 1) / T - 1;
+    const int64_t p_last = (b * P + T - 1) / T - 1;
+    const int ncontrib = (int)(p_last - p_first + 1);
+    // Slot of a share's partial for this row: 1 in the share where the row
+    // begins (p_first: the row is its last), 0 in every later share (the
+    // row began before the share: it is the share's first).
+    auto slot_of = [&](int64_t c) { return c == p_first ? 1 : 0; };
+
+    acc.init();
+    const int nk_all = (j_hi - j_lo > sub) ? (j_hi - j_lo - 1 - sub) / Ssub + 1 : 0;
+    if (head_ok && nk_all > 0) {
+      bf16x8 qv[Sh::kKChunks];
+      load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G);
+      const uint16_t* kbase = k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row;
+      const uint16_t* vbase = v_cache + (int64_t)g * D;
+      const int32_t* trow = block_table + (int64_t)s * MB + j_lo + sub;
+      for (int kc = 0; kc < nk_all; kc += kWave) {
+        const int nk = min(kWave, nk_all - kc);
+        const int ids = lane < nk ? trow[(int64_t)(kc + lane) * Ssub] : 0;
+        stream_blocks<D, NBUF, kStreamV>(acc, qv, ids, nk, (j_lo + sub + kc * Ssub) * kBlock,
+                                         Ssub * kBlock, L, kbase, vbase, kv_row, vl, scale_log2,
+                                         lane);
+      }
+      acc.lsum = sum_across_groups(acc.lsum);
+    }
+
+    const int my_slot = slot_of(p);
+    merge_waves<D>(acc, stage, W, HG, G, w, lane,
+                   [&](int sl, int col, int d, float M, float den, float n0, float n1) {
+      const int head = blockIdx.y * HG + sl;
+      if (head >= Hkv) return;
+      const int qh = head * G + col;
+      if (ncontrib == 1) {
+        const float inv = 1.0f / den;
+        *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+      } else {  // read by the share that finishes this row last
+        const int64_t row = ((int64_t)p * 2 + my_slot) * Hq + qh;
+        store_coherent2(ws_o + row * D + d, n0, n1);
+        if (d == 0) store_coherent2(ws_ml + row * 2, M, den);
+      }
+    });
+
+    if (ncontrib > 1) {
+      // Publish: this workgroup's partial stores have completed before it
+      // counts itself in; the last to count in merges every share's partial
+      // in share order and leaves the counter at zero for the next call.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int32_t* ctr = counters + (int64_t)s * gridDim.y + blockIdx.y;
+        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == ncontrib - 1;
+        if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+      }
+      __syncthreads();
+      if (*flag) {
+        // Online merge in share order, eight shares' loads in flight at a
+        // time; every share's partial covers a block with a visible token,
+        // so each m is finite.
+        const int per_head = G * (D / 2);
+        for (int idx = threadIdx.x; idx < HG * per_head; idx += blockDim.x) {
+          const int head = blockIdx.y * HG + idx / per_head;
+          if (head >= Hkv) continue;
+          const int qh = head * G + (idx % per_head) / (D / 2);
+          const int d = 2 * (idx % (D / 2));
+          float M = -INFINITY, den = 0.f, n0 = 0.f, n1 = 0.f;
+          for (int64_t c0 = p_first; c0 <= p_last; c0 += 8) {
+            f32x2 ml[8], ov[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int64_t c = min(c0 + k, p_last);
+              const int64_t row = (c * 2 + slot_of(c)) * Hq + qh;
+              ml[k] = load_coherent2(ws_ml + row * 2);
+              ov[k] = load_coherent2(ws_o + row * D + d);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              if (c0 + k <= p_last) {
+                const float mn = fmaxf(M, ml[k][0]);
+                const float sc = fast_exp2(M - mn);
+                const float e = fast_exp2(ml[k][0] - mn);
+                den = den * sc + e * ml[k][1];
+                n0 = n0 * sc + e * ov[k][0];
+                n1 = n1 * sc + e * ov[k][1];
+                M = mn;
+              }
+            }
+          }
+          const float inv = 1.0f / den;
+          *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partitioned schedule
+// ---------------------------------------------------------------------------
+
 template <int D, int NBUF, bool kStreamV>
 __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
@@ -93,8 +515,6 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
 
   const int lane = threadIdx.x & (kWave - 1);
-  // The wave index is uniform across the wave; saying so keeps the block
-  // loop and the table reads on scalar registers.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int W = blockDim.x / kWave;
   // Rows vary fastest in the grid: consecutive workgroups are dealt to the
@@ -121,178 +541,34 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   const int nparts = (L + part_tokens - 1) / part_tokens;
   const int nblk = (tok_end + kBlock - 1) / kBlock - b_begin;
   const int nmine = nblk > w ? (nblk - 1 - w) / W + 1 : 0;  // blocks of this wave
+  const int hl = lane & 15;
+  const int grp = lane >> 4;
+  const int64_t kv_row = (int64_t)Hkv * D;
 
-  const int hl = lane & 15;   // head within the group (MFMA column)
-  const int grp = lane >> 4;  // 16-lane group
-  const int64_t kv_row = (int64_t)Hkv * D;  // elements between consecutive tokens of a block
-
-  f32x4 o[Sh::kDTiles];
-#pragma unroll
-  for (int mi = 0; mi < Sh::kDTiles; ++mi) o[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY;
-  float lsum = 0.f;
-
+  WaveAcc<D> acc;
+  acc.init();
   if (nmine > 0) {
-    // Q^T as the B operand: lane holds head hl, d = 32*i + 8*grp + e.
     bf16x8 qv[Sh::kKChunks];
-    {
-      const u32x4* qp = (const u32x4*)(q + ((int64_t)t0 * Hq + g * G + hl) * D) + grp;
-#pragma unroll
-      for (int i = 0; i < Sh::kKChunks; ++i) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        qv[i] = as_bf16x8(hl < G ? qp[4 * i] : z);
-      }
-    }
-    uint16_t* vl = lds + w * Sh::kLdsWave;
-    const uint16_t* kbase = k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row;
-    const uint16_t* vbase = v_cache + (int64_t)g * D;
-
-    // Loads the wave's block min(k, nmine-1): always issued, so the wait
-    // counts stay exact. Unless blocks are shared between rows, V goes
-    // through nontemporal (streaming) loads: each V load covers whole rows
-    // and is read once, and measured faster that way. K keeps plain loads:
-    // two of its loads cover the two halves of one 128-byte line, which
-    // streaming loads re-fetch.
-    auto load_block = [&](int k, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
-      const int64_t blk = __builtin_amdgcn_readlane(my_blk, min(k, nmine - 1));
-      const int64_t boff = blk * kBlock * kv_row;
-      const u32x4* kp = (const u32x4*)(kbase + boff);
-#pragma unroll
-      for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = kp[4 * i];
-#pragma unroll
-      for (int c = 0; c < Sh::kVChunks; ++c) {
-        const int idx = c * kWave + lane;
-        const int row = idx / (D / 8);
-        const int col8 = idx % (D / 8);
-        const u32x4* vp = (const u32x4*)(vbase + boff + row * kv_row + col8 * 8);
-        vv[c] = kStreamV ? __builtin_nontemporal_load(vp) : *vp;
-      }
-    };
-
-    auto process_block = [&](int k, const u32x4 (&kk)[Sh::kKChunks],
-                             const u32x4 (&vv)[Sh::kVChunks]) {
-      const int tokb = (b_begin + w + k * W) * kBlock;
-      // V block into this wave's LDS slice, rows past the sequence zeroed.
-#pragma unroll
-      for (int c = 0; c < Sh::kVChunks; ++c) {
-        const int idx = c * kWave + lane;
-        const int row = idx / (D / 8);
-        const int col8 = idx % (D / 8);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *(u32x4*)(vl + row * Sh::kLdsRow + col8 * 8) = (tokb + row < L) ? vv[c] : z;
-      }
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < Sh::kKChunks; ++i) sacc = mfma_16x16x32(as_bf16x8(kk[i]), qv[i], sacc);
-      float sv[4];
-      bool over = false;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = tokb + 4 * grp + r;
-        sv[r] = tok < tok_end ? sacc[r] * scale_log2 : -INFINITY;
-        over |= sv[r] > m + kLazy;
-      }
-      if (__any(over)) {  // wave-uniform: re-reference the softmax
-        float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-        bm = max_across_groups(bm);
-        const float mn = fmaxf(m, bm);
-        const float alpha = fast_exp2(m - mn);
-        lsum *= alpha;
-#pragma unroll
-        for (int mi = 0; mi < Sh::kDTiles; ++mi) o[mi] *= alpha;
-        m = mn;
-      }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(sv[r] - m);
-        lsum += p[r];
-      }
-      const u32x2 s01 = split_pack_bf16x2(p[0], p[1]);
-      const u32x2 s23 = split_pack_bf16x2(p[2], p[3]);
-      const i16x4 phi = __builtin_bit_cast(i16x4, u32x2{s01[0], s23[0]});
-      const i16x4 plo = __builtin_bit_cast(i16x4, u32x2{s01[1], s23[1]});
-      wave_lds_fence();
-      // A operand V^T[d = 16*mi + hl][token 4*grp + r] by transpose reads.
-      const uint16_t* vrow = vl + (4 * grp + hl / 4) * Sh::kLdsRow + 4 * (hl % 4);
-#pragma unroll
-      for (int mi = 0; mi < Sh::kDTiles; ++mi) {
-        const i16x4 a = lds_read_tr16(vrow + 16 * mi);
-        o[mi] = mfma_16x16x16(a, phi, o[mi]);
-        o[mi] = mfma_16x16x16(a, plo, o[mi]);
-      }
-      wave_lds_fence();
-    };
-
-    // The main loop runs whole rounds of NBUF blocks with no early exit, so
-    // the loads still in flight at its back-edge are always the same NBUF-1
-    // ring slots in the same order and every wait is for exactly the block
-    // being consumed (an exit inside the round makes the wait at the loop
-    // head drain all loads). Block k0 + v of the last partial round already
-    // sits in slot v.
-    u32x4 kb[NBUF][Sh::kKChunks], vb[NBUF][Sh::kVChunks];
-#pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u) load_block(u, kb[u], vb[u]);
-    int k0 = 0;
-    for (; k0 + NBUF <= nmine; k0 += NBUF) {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        load_block(k0 + u + NBUF - 1, kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF]);
-        process_block(k0 + u, kb[u], vb[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u)
-      if (k0 + u < nmine) process_block(k0 + u, kb[u], vb[u]);
-    lsum = sum_across_groups(lsum);
+    load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G);
+    stream_blocks<D, NBUF, kStreamV>(
+        acc, qv, my_blk, nmine, (b_begin + w) * kBlock, W * kBlock, tok_end,
+        k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row, v_cache + (int64_t)g * D,
+        kv_row, lds + w * Sh::kLdsWave, scale_log2, lane);
+    acc.lsum = sum_across_groups(acc.lsum);
   }
 
-  // Merge the W waves' states through LDS (the V slices are free once every
-  // wave has passed the barrier), kMergeHeads heads per pass:
-  //   M = max_w m_w, l = sum_w 2^(m_w - M) l_w, o = sum_w 2^(m_w - M) o_w,
-  // in wave order (deterministic). A wave without blocks holds m = -inf,
-  // l = 0, o = 0 and adds nothing; wave 0 always has a block.
-  float* mo = (float*)lds;                                       // [W][8][D + 4]
-  float* mml = mo + (size_t)W * Sh::kMergeHeads * Sh::kMergeRow;  // [W][8][2]
-  for (int hb = 0; hb < G; hb += Sh::kMergeHeads) {
-    __syncthreads();
-    const int hh = hl - hb;
-    if (hl < G && hh >= 0 && hh < Sh::kMergeHeads) {
-      float* orow = mo + (w * Sh::kMergeHeads + hh) * Sh::kMergeRow + 4 * grp;
-#pragma unroll
-      for (int mi = 0; mi < Sh::kDTiles; ++mi) *(f32x4*)(orow + 16 * mi) = o[mi];
-      if (grp == 0) {
-        mml[(w * Sh::kMergeHeads + hh) * 2 + 0] = m;
-        mml[(w * Sh::kMergeHeads + hh) * 2 + 1] = lsum;
-      }
+  merge_waves<D>(acc, (float*)lds, W, 1, G, w, lane,
+                 [&](int, int col, int d, float M, float den, float n0, float n1) {
+    const int qh = g * G + col;
+    if (nparts == 1) {
+      const float inv = 1.0f / den;
+      *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+    } else {  // read by the combine kernel after this one ends
+      const int64_t base = ((int64_t)s * num_parts_max + part) * Hq + qh;
+      *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
+      if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
     }
-    __syncthreads();
-    const int nh = min(Sh::kMergeHeads, G - hb);
-    for (int idx = threadIdx.x; idx < nh * (D / 2); idx += blockDim.x) {
-      const int h = idx / (D / 2);
-      const int d = 2 * (idx % (D / 2));
-      float M = -INFINITY;
-      for (int v = 0; v < W; ++v) M = fmaxf(M, mml[(v * Sh::kMergeHeads + h) * 2]);
-      float den = 0.f, n0 = 0.f, n1 = 0.f;
-      for (int v = 0; v < W; ++v) {
-        const float* ml = mml + (v * Sh::kMergeHeads + h) * 2;
-        const float e = fast_exp2(ml[0] - M);
-        const float* orow = mo + (v * Sh::kMergeHeads + h) * Sh::kMergeRow + d;
-        den += e * ml[1];
-        n0 += e * orow[0];
-        n1 += e * orow[1];
-      }
-      const int head = g * G + hb + h;
-      if (nparts == 1) {
-        const float inv = 1.0f / den;
-        *(uint32_t*)(out + ((int64_t)t0 * Hq + head) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
-      } else {  // read by the combine kernel after this one ends
-        const int64_t base = ((int64_t)s * num_parts_max + part) * Hq + head;
-        *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
-        if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
-      }
-    }
-  }
+  });
 }
 
 // Merge of a row's partitions: one wave per (row, head), lanes across d,
@@ -365,6 +641,22 @@ template <int D, int NBUF, bool kStreamV>
 hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
   using Sh = DecodeShape<D>;
   const float scale_log2 = a.scale * 1.4426950408889634f;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (p.stream) {
+    const int groups = (a.num_kv_heads + p.stream_heads - 1) / p.stream_heads;
+    dim3 grid(p.stream_wgs, groups);
+    const size_t lds = (size_t)p.waves * Sh::kLdsWave * sizeof(uint16_t) +
+                       ((size_t)a.num_seqs + 1 + 17 + 1) * sizeof(int32_t);
+    profile_begin(PA_KERNEL_DECODE, stream);
+    hipLaunchKernelGGL((decode_stream_kernel<D, NBUF, kStreamV>), grid, dim3(p.waves * kWave),
+                       lds, stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                       (const uint16_t*)a.v_cache, a.block_table, a.seq_lens,
+                       a.query_start_loc, (uint16_t*)a.out, p.ws_o, p.ws_ml, p.counters,
+                       scale_log2, a.num_q_heads, a.num_kv_heads, G, a.max_blocks_per_seq,
+                       a.num_seqs, p.stream_heads);
+    profile_end(PA_KERNEL_DECODE, stream);
+    return hipGetLastError();
+  }
   dim3 grid(a.num_seqs, a.num_kv_heads, p.num_parts_max);
   const size_t lds = (size_t)p.waves * Sh::kLdsWave * sizeof(uint16_t);
   profile_begin(PA_KERNEL_DECODE, stream);
@@ -373,8 +665,7 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                      (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                      (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
-                     a.num_kv_heads, a.num_q_heads / a.num_kv_heads, a.max_blocks_per_seq,
-                     p.part_tokens, p.num_parts_max);
+                     a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max);
   profile_end(PA_KERNEL_DECODE, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_parts_max <= 1) return e;
@@ -397,14 +688,24 @@ int32_t decode_max_waves(int32_t head_size, int32_t prefetch) {
   }
 }
 
+size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seqs) {
+  const size_t slice = head_size == 64 ? DecodeShape<64>::kLdsWave : DecodeShape<128>::kLdsWave;
+  return (size_t)waves * slice * sizeof(uint16_t) + ((size_t)num_seqs + 1 + 17 + 1) * 4;
+}
+
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
   const int maxw = decode_max_waves(a.head_size, p.prefetch);
-  if (p.waves < 1 || p.waves > maxw || p.part_tokens <= 0 || p.part_tokens % kBlock ||
-      p.part_tokens / kBlock > kWave * p.waves || p.num_parts_max > 65535 ||
-      a.num_kv_heads > 65535)
+  if (p.waves < 1 || p.waves > maxw || a.num_kv_heads > 65535) return hipErrorInvalidValue;
+  if (p.stream) {
+    if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||
+        decode_stream_lds_bytes(a.head_size, p.waves, a.num_seqs) > 64 * 1024)
+      return hipErrorInvalidValue;
+  } else if (p.part_tokens <= 0 || p.part_tokens % kBlock ||
+             p.part_tokens / kBlock > kWave * p.waves || p.num_parts_max > 65535) {
     return hipErrorInvalidValue;
-  // Ring depths that fit the register budget of kMaxWaves waves per CU
-  // without spills: 2 or 3 blocks at D = 64, 2 at D = 128.
+  }
+  // Ring depths that fit the register budget without spills: 2 or 3 blocks
+  // at D = 64, 2 at D = 128.
   const bool sv = p.stream_v;
   switch (a.head_size) {
     case 64:

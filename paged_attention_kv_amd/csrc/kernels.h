@@ -32,21 +32,31 @@ struct ForwardArgs {
   int32_t max_query_len, max_seq_len;  // resolved upper bounds (hints or defaults)
 };
 
-// Decode rows (q_len == 1): one workgroup per (row, KV head, partition);
-// direct output for rows of one partition, else partials and a combine.
+// Decode rows (q_len == 1). Stream schedule: stream_wgs workgroups each take
+// an equal share of all decode rows' blocks, stream_heads KV heads per
+// workgroup (grid y covers the rest), waves / stream_heads waves per head;
+// rows split between shares are merged by the last share through counters.
+// Partitioned schedule: one workgroup per (row, KV head, partition); rows of
+// several partitions are merged by a combine kernel.
 struct DecodePlan {
-  int32_t part_tokens;    // tokens per partition (multiple of 16, <= 1024 * waves)
-  int32_t num_parts_max;  // partitions per row (grid z, <= 65535; workspace stride)
+  bool stream;            // stream schedule (else partitioned)
+  int32_t stream_wgs;     // stream: workgroups (grid x)
+  int32_t stream_heads;   // stream: KV heads per workgroup (divides waves)
+  int32_t part_tokens;    // partitioned: tokens per partition (multiple of 16)
+  int32_t num_parts_max;  // partitioned: partitions per row (grid z; workspace stride)
   int32_t waves;          // waves per workgroup (1..decode_max_waves)
   int32_t prefetch;       // register ring depth in 16-token blocks (2, or 3 at D = 64)
   bool stream_v;          // V through nontemporal loads (blocks not shared)
-  float* ws_o;            // [S][num_parts_max][Hq][D] unnormalised partial outputs
-  float* ws_ml;           // [S][num_parts_max][Hq][2] reference max (log2 units) and sum
+  float* ws_o;            // partial outputs: stream [wgs][2][Hq][D], partitioned [S][parts][Hq][D]
+  float* ws_ml;           // partial (max in log2 units, sum): same rows, 2 floats each
+  int32_t* counters;      // stream: [S][groups] arrival counters, zero between calls
 };
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream);
 // Most waves a decode workgroup may hold for this head size and ring depth
 // (0: head size not built).
 int32_t decode_max_waves(int32_t head_size, int32_t prefetch);
+// LDS bytes of one stream-schedule workgroup.
+size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seqs);
 
 // Prefill rows (q_len > 1): a planner writes the tile list, then the tiles run.
 struct PrefillPlan {
@@ -65,8 +75,10 @@ int32_t prefill_split_tiles_per_row(int32_t group);
 
 // Workspace layout shared by pa_forward and pa_forward_workspace_bytes.
 struct WorkspaceLayout {
+  bool stream;
+  int32_t stream_wgs, stream_heads, waves, prefetch;
   int32_t part_tokens, num_parts_max, tile_queries, bound_a, bound_b;
-  size_t off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
+  size_t off_ctr, off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
 };
 bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,

@@ -41,6 +41,21 @@ constexpr int32_t kBalancePartTokens = 4096;
 constexpr int32_t kComputeUnits = 256;  // MI355X
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxGridZ = 65535;  // partitions per row ride on grid z
+// Row arrival counters of the stream decode schedule: a region of fixed size
+// at the start of every workspace, zero before the first call and left zero
+// by every call, so no call of any shape writes other data over them.
+constexpr int64_t kCounterSlots = 1 << 16;
+// Stream decode schedule: at most this many rows (each workgroup scans them
+// all in LDS), this many workgroups, and this many waves per workgroup
+// (one per KV head of a head group, or several per head when heads are few).
+constexpr int32_t kStreamMaxRows = 4096;
+constexpr int32_t kStreamMaxWgs = 512;
+constexpr int32_t kStreamWaves = 8;
+// The stream schedule pays a fixed latency per workgroup (row scan, first
+// loads, hand-over of split rows) while HBM idles; it wins once a share is
+// long enough to hide it. Shares are estimated from host bounds (rows x
+// blocks of the longest row).
+constexpr int64_t kStreamMinBlocksPerWg = 64;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -91,6 +106,29 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t waves
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
+// Decode schedule: the stream schedule (equal shares of all rows' blocks per
+// workgroup) when shares would be long enough and the batch has few enough
+// rows for its per-workgroup row scan, else the partitioned one.
+// PA_DECODE_STREAM=0 / 1 forces partitioned / stream (where it fits);
+// PA_DECODE_STREAM_WGS sets the stream workgroups (default one per CU).
+int32_t decode_stream_wgs();
+bool decode_use_stream(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
+                       int32_t max_len) {
+  static const int env = env_int("PA_DECODE_STREAM", 0, 2, 2);  // 2: by size
+  if (!env || num_seqs > kStreamMaxRows) return false;
+  const int64_t blocks_bound = (int64_t)num_seqs * ((max_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE);
+  if (env == 2 && blocks_bound < kStreamMinBlocksPerWg * decode_stream_wgs()) return false;
+  const int32_t heads = std::min(num_kv_heads, kStreamWaves);
+  const int64_t groups = (num_kv_heads + heads - 1) / heads;
+  return (int64_t)num_seqs * groups <= kCounterSlots &&
+         pa::decode_stream_lds_bytes(head_size, kStreamWaves / heads * heads, num_seqs) <=
+             64 * 1024;
+}
+int32_t decode_stream_wgs() {
+  static const int v = env_int("PA_DECODE_STREAM_WGS", 1, kStreamMaxWgs, kComputeUnits);
+  return v;
+}
+
 // Register ring depth of the decode kernel (blocks in flight per wave);
 // PA_DECODE_PREFETCH overrides it for tuning sweeps.
 int32_t decode_prefetch(int32_t head_size) {
@@ -113,21 +151,40 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   if (!supported_group(group)) return false;
   const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
   WorkspaceLayout w;
-  w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads,
-                                     decode_waves(head_size, decode_prefetch(head_size)), max_len);
-  // Reserve for the smallest partition size so any tuning choice fits.
-  w.num_parts_max = (max_len + kMinPartTokens - 1) / kMinPartTokens;
-  if (w.num_parts_max > kMaxGridZ) return false;
+  w.prefetch = decode_prefetch(head_size);
+  w.stream = decode_use_stream(num_seqs, num_kv_heads, head_size, max_len);
+  size_t dec_o = 0, dec_ml = 0;  // fp32 elements of the decode partials
+  if (w.stream) {
+    w.stream_heads = std::min(num_kv_heads, kStreamWaves);
+    w.waves = kStreamWaves / w.stream_heads * w.stream_heads;
+    w.stream_wgs = decode_stream_wgs();
+    w.part_tokens = 0;
+    w.num_parts_max = 0;
+    const size_t rows = (size_t)w.stream_wgs * 2 * num_q_heads;  // (share, slot, head)
+    dec_o = rows * head_size;
+    dec_ml = rows * 2;
+  } else {
+    w.stream_heads = 0;
+    w.stream_wgs = 0;
+    w.waves = decode_waves(head_size, w.prefetch);
+    w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, w.waves, max_len);
+    w.num_parts_max = (max_len + w.part_tokens - 1) / w.part_tokens;
+    if (w.num_parts_max > kMaxGridZ) return false;
+    const size_t rows =
+        w.num_parts_max > 1 ? (size_t)num_seqs * w.num_parts_max * num_q_heads : 0;
+    dec_o = rows * head_size;
+    dec_ml = rows * 2;
+  }
   w.tile_queries = prefill_tile_queries(group);
   // Each row adds at most one partial tile: sum ceil(ql/BQ) <= T/BQ + S.
   const int64_t any_bound = (int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
   w.bound_a = (int32_t)any_bound;
   w.bound_b = (int32_t)std::min<int64_t>(
       any_bound, (int64_t)num_seqs * prefill_split_tiles_per_row(group));
-  const size_t rows = (size_t)num_seqs * w.num_parts_max * num_q_heads;
-  w.off_o = 0;
-  w.off_ml = round_up(w.off_o + rows * head_size * sizeof(float), kAlign);
-  w.off_counts = round_up(w.off_ml + rows * 2 * sizeof(float), kAlign);
+  w.off_ctr = 0;
+  w.off_o = round_up((size_t)kCounterSlots * sizeof(int32_t), kAlign);
+  w.off_ml = round_up(w.off_o + dec_o * sizeof(float), kAlign);
+  w.off_counts = round_up(w.off_ml + dec_ml * sizeof(float), kAlign);
   w.off_tiles_a = w.off_counts + kAlign;
   w.off_tiles_b = round_up(w.off_tiles_a + (size_t)w.bound_a * 2 * sizeof(int32_t), kAlign);
   w.total = round_up(w.off_tiles_b + (size_t)w.bound_b * 2 * sizeof(int32_t), kAlign);
@@ -276,13 +333,17 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
     if (e != hipSuccess) return hip_fail(e, "pa_forward prefill launch");
   }
   pa::DecodePlan dp;
+  dp.stream = w.stream;
+  dp.stream_wgs = w.stream_wgs;
+  dp.stream_heads = w.stream_heads;
   dp.part_tokens = w.part_tokens;
-  dp.num_parts_max = (a.max_seq_len + w.part_tokens - 1) / w.part_tokens;
-  dp.prefetch = decode_prefetch(head_size);
-  dp.waves = decode_waves(head_size, dp.prefetch);
+  dp.num_parts_max = w.num_parts_max;
+  dp.prefetch = w.prefetch;
+  dp.waves = w.waves;
   dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
+  dp.counters = (int32_t*)(ws + w.off_ctr);
   hipError_t e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward decode launch");
   return PA_OK;

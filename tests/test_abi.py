@@ -109,15 +109,30 @@ def test_workspace_sizes_for_the_named_workloads(lib, i):
     s = wl.config(i)
     n = pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads, s.num_kv_heads,
                                    s.head_size, s.max_blocks_per_seq)
-    # split-K partials of every row at the smallest partition (128 tokens)
-    parts = -(-s.max_blocks_per_seq * 16 // 128)
-    assert n >= s.num_seqs * parts * s.num_q_heads * (s.head_size + 2) * 4
+    # the counter region, then (when rows may be split) decode partials
+    assert n > pa.WORKSPACE_COUNTER_BYTES
     assert n % 256 == 0
     assert n < 512 << 20
     # a tighter max_seq_len hint never needs more
     n2 = pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads, s.num_kv_heads,
                                     s.head_size, s.max_blocks_per_seq, max(s.seq_lens))
     assert n2 <= n
+
+
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define PA_BLOCK_SIZE (\d+)", text).group(1)) == pa.BLOCK_SIZE
+    assert int(re.search(r"#define PA_FORWARD_SHARED_BLOCKS (\d+)u", text).group(1)) == \
+        pa.FORWARD_SHARED_BLOCKS
+    m = re.search(r"#define PA_WORKSPACE_COUNTER_BYTES \((\d+)u \* (\d+)u\)", text)
+    assert int(m.group(1)) * int(m.group(2)) == pa.WORKSPACE_COUNTER_BYTES
+
+
+def test_workspace_starts_with_the_counter_region(lib):
+    # any shape needs at least the counter region, 256-byte aligned sizes
+    for args in ((64, 64, 32, 4, 64, 128, 0), (8192, 260, 32, 8, 128, 512, 0), (1, 1, 8, 8, 128, 1, 0)):
+        n = pa.forward_workspace_bytes(*args)
+        assert n > pa.WORKSPACE_COUNTER_BYTES and n % 256 == 0
 
 
 def test_profile_with_no_launches_is_empty(lib):

@@ -214,6 +214,44 @@ def test_long_context_split_into_many_partitions(part):
     assert_close(out.cpu()[r], want, "longsplit")
 
 
+# Decode-row schedules: the stream schedule shares all rows' blocks out
+# evenly over one workgroup per CU (rows cut by a share are merged by the
+# share that finishes them last); batches of more than 4096 rows take the
+# partitioned schedule.
+DECODE_SCHEDULE_CASES = [
+    # two long rows cut into ~128 shares each
+    ("split_long", 64, 8, 128, [(1, 30000), (1, 29990)]),
+    # thousands of short rows, many rows per share, lengths 1..40
+    ("many_short", 32, 4, 64, [(1, (7 * i) % 40) for i in range(3000)]),
+    # fewer blocks than workgroups: a share per block
+    ("few_blocks", 32, 8, 128, [(1, 4), (1, 20), (1, 0)]),
+    # 16 KV heads: two head groups along the grid
+    ("kv16", 16, 16, 64, [(1, 300), (1, 1000), (1, 77)]),
+    # one KV head for 16 query heads: eight waves per head
+    ("mqa16", 16, 1, 128, [(1, 2000), (1, 500), (1, 3)]),
+    # decode rows between prefill rows (rows without blocks in the scan)
+    ("interleaved", 32, 8, 128, [(5, 100), (1, 900), (17, 0), (1, 33), (2, 2000), (1, 4100)]),
+    # more than 4096 rows: partitioned schedule
+    ("partitioned", 16, 4, 64, [(1, 3 + (i % 37)) for i in range(4200)]),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,rows", DECODE_SCHEDULE_CASES,
+                         ids=[c[0] for c in DECODE_SCHEDULE_CASES])
+def test_decode_schedules(name, hq, hkv, d, rows):
+    spec = wl.custom(name, hq, hkv, d, rows=rows, seed=60 + len(rows) % 97)
+    banner(f"decode schedule {name}: S={spec.num_seqs} Hq={hq} Hkv={hkv} D={d}")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case)
+    out2 = write_and_forward(case).clone()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
+    if len(seqs) > 64:
+        seqs = seqs[:16] + seqs[len(seqs) // 2 - 8:len(seqs) // 2 + 8] + seqs[-16:]
+    r, want = oracle_rows(case, seqs)
+    assert_close(out.cpu()[r], want, name)
+
+
 def test_nan_poison_outside_context_does_not_leak():
     rows = [(1, 18), (7, 9), (1, 31), (40, 0), (1, 1)]
     spec = wl.custom("nanpoison", 32, 8, 128, rows=rows, seed=42)
@@ -305,16 +343,18 @@ def test_validate_inputs_accepts_good_and_names_bad_metadata():
 
 
 def test_workspace_shared_by_calls_of_different_shapes():
-    """One workspace, filled with 0xFF bytes (NaN as fp32) before the first
-    call, serves calls whose split-K layouts differ: few partitions and many
-    rows, then many partitions and few rows, alternately. Every call must
-    write what it reads (the workspace may hold anything between calls)."""
+    """One workspace serves calls whose decode layouts differ (many short
+    rows, then two long rows split between many workgroups), alternately.
+    Past the counter region it is filled with 0xFF bytes (NaN as fp32) before
+    the first call: every call writes what it reads there. The counter region
+    starts at zero and must be zero again after every call."""
     few = wl.custom("ws_few", 32, 8, 128, rows=[(1, 4000)] * 40, seed=47)
     many = wl.custom("ws_many", 64, 8, 128, rows=[(1, 30000), (1, 20000)], seed=48)
     nbytes = max(pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads,
                                             s.num_kv_heads, s.head_size, s.max_blocks_per_seq)
                  for s in (few, many))
     ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    ws[:pa.WORKSPACE_COUNTER_BYTES].zero_()
     for spec in (few, many, few, many, few):
         banner(f"workspace reuse: {spec.name}")
         case = wl.make_case(spec, device=DEV)
@@ -322,6 +362,7 @@ def test_workspace_shared_by_calls_of_different_shapes():
         pick = list(range(0, spec.num_seqs, max(1, spec.num_seqs // 6)))
         r, want = oracle_rows(case, pick)
         assert_close(out.cpu()[r], want, spec.name)
+        assert int(ws[:pa.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, "counters left nonzero"
 
 
 def test_kernel_timing_records_each_launch_class():
