@@ -164,9 +164,19 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
  *       streaming (nontemporal) loads, the faster choice for blocks read once.
  *       Either way the results are identical.
  *
- * Unknown flag bits return PA_ERR_UNSUPPORTED.
+ *   PA_FORWARD_DECODE_EVEN_SHARES, PA_FORWARD_DECODE_PARTITIONED
+ *       force the decode rows' schedule: every workgroup takes an equal share
+ *       of all rows' blocks (rows cut by a share are merged by the share that
+ *       finishes them last), or rows are split into fixed partitions merged
+ *       by a combine pass. Without either the library picks by batch size.
+ *       EVEN_SHARES falls back to partitions when num_seqs > 4096. The
+ *       results agree to rounding order; each schedule is deterministic.
+ *
+ * Unknown flag bits, or both schedule flags, return PA_ERR_UNSUPPORTED.
  */
 #define PA_FORWARD_SHARED_BLOCKS 1u
+#define PA_FORWARD_DECODE_EVEN_SHARES 2u
+#define PA_FORWARD_DECODE_PARTITIONED 4u
 
 int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, const int32_t* seq_lens,

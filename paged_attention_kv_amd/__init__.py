@@ -23,6 +23,9 @@ __all__ = ["cache_write", "forward", "forward_workspace_bytes", "validate_inputs
 BLOCK_SIZE = 16
 FORWARD_SHARED_BLOCKS = 1  # PA_FORWARD_SHARED_BLOCKS
 WORKSPACE_COUNTER_BYTES = 256 * 1024  # PA_WORKSPACE_COUNTER_BYTES
+FORWARD_DECODE_EVEN_SHARES = 2  # PA_FORWARD_DECODE_EVEN_SHARES
+FORWARD_DECODE_PARTITIONED = 4  # PA_FORWARD_DECODE_PARTITIONED
+_SCHEDULE_FLAGS = {"even": FORWARD_DECODE_EVEN_SHARES, "partitioned": FORWARD_DECODE_PARTITIONED}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
 _lib = None
@@ -175,15 +178,17 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             scale: float, out: Optional[torch.Tensor] = None,
             max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
             workspace: Optional[torch.Tensor] = None,
-            shared_blocks: bool = False) -> torch.Tensor:
+            shared_blocks: bool = False,
+            decode_schedule: Optional[str] = None) -> torch.Tensor:
     """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
     paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
     ``max_seq_len`` are optional host upper bounds that shrink the launch
     grids; ``workspace`` (uint8, on the device, its first
     ``WORKSPACE_COUNTER_BYTES`` zero before its first use) is taken from a
-    per-device cache when omitted. ``shared_blocks``
-    tells the library that some blocks appear in several rows' tables
-    (prefix caching); results are the same either way."""
+    per-device cache when omitted. ``shared_blocks`` tells the library that
+    some blocks appear in several rows' tables (prefix caching); results are
+    the same either way. ``decode_schedule`` ("even" or "partitioned")
+    forces the decode rows' schedule; by default the library picks."""
     lib = load_library()
     _dev_tensor("q", q, torch.bfloat16, 3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -204,6 +209,11 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _dev_tensor("out", out, torch.bfloat16, 3)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
+    flags = FORWARD_SHARED_BLOCKS if shared_blocks else 0
+    if decode_schedule is not None:
+        if decode_schedule not in _SCHEDULE_FLAGS:
+            raise ValueError(f"decode_schedule must be one of {sorted(_SCHEDULE_FLAGS)}")
+        flags |= _SCHEDULE_FLAGS[decode_schedule]
     need = lib.pa_forward_workspace_bytes(T, S, Hq, Hkv, D, MB, max_seq_len or 0)
     if workspace is None:
         workspace = _workspace(q.device, need)
@@ -214,7 +224,7 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                              query_start_loc.data_ptr(), float(scale), out.data_ptr(), T, S, Hq,
                              Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             FORWARD_SHARED_BLOCKS if shared_blocks else 0, _stream(q)))
+                             flags, _stream(q)))
     return out
 
 

@@ -75,8 +75,8 @@ int32_t prefill_split_tiles_per_row(int32_t group);
 
 // Workspace layout shared by pa_forward and pa_forward_workspace_bytes.
 struct WorkspaceLayout {
-  bool stream;
-  int32_t stream_wgs, stream_heads, waves, prefetch;
+  bool stream_ok, stream_default;  // even shares fit / are the default schedule
+  int32_t stream_wgs, stream_heads, stream_waves, waves, prefetch;
   int32_t part_tokens, num_parts_max, tile_queries, bound_a, bound_b;
   size_t off_ctr, off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
 };

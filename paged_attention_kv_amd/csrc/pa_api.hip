@@ -106,27 +106,30 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t waves
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
-// Decode schedule: the stream schedule (equal shares of all rows' blocks per
-// workgroup) when shares would be long enough and the batch has few enough
-// rows for its per-workgroup row scan, else the partitioned one.
-// PA_DECODE_STREAM=0 / 1 forces partitioned / stream (where it fits);
-// PA_DECODE_STREAM_WGS sets the stream workgroups (default one per CU).
-int32_t decode_stream_wgs();
-bool decode_use_stream(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
-                       int32_t max_len) {
-  static const int env = env_int("PA_DECODE_STREAM", 0, 2, 2);  // 2: by size
-  if (!env || num_seqs > kStreamMaxRows) return false;
-  const int64_t blocks_bound = (int64_t)num_seqs * ((max_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE);
-  if (env == 2 && blocks_bound < kStreamMinBlocksPerWg * decode_stream_wgs()) return false;
+// Decode schedules. Even shares (the stream kernel: equal shares of all
+// rows' blocks per workgroup) fit when the batch has few enough rows for the
+// per-workgroup row scan; they are the default when shares would be long
+// enough, else the partitioned schedule is. PA_DECODE_STREAM=0 / 1 makes the
+// default partitioned / even shares (where they fit); PA_DECODE_STREAM_WGS
+// sets the even-share workgroups (default one per CU). Per call, flags of
+// pa_forward_ex choose.
+int32_t decode_stream_wgs() {
+  static const int v = env_int("PA_DECODE_STREAM_WGS", 1, kStreamMaxWgs, kComputeUnits);
+  return v;
+}
+bool decode_stream_fits(int32_t num_seqs, int32_t num_kv_heads, int32_t head_size) {
+  if (num_seqs > kStreamMaxRows) return false;
   const int32_t heads = std::min(num_kv_heads, kStreamWaves);
   const int64_t groups = (num_kv_heads + heads - 1) / heads;
   return (int64_t)num_seqs * groups <= kCounterSlots &&
          pa::decode_stream_lds_bytes(head_size, kStreamWaves / heads * heads, num_seqs) <=
              64 * 1024;
 }
-int32_t decode_stream_wgs() {
-  static const int v = env_int("PA_DECODE_STREAM_WGS", 1, kStreamMaxWgs, kComputeUnits);
-  return v;
+bool decode_stream_default(int32_t num_seqs, int32_t max_len) {
+  static const int env = env_int("PA_DECODE_STREAM", 0, 2, 2);  // 2: by size
+  if (env != 2) return env == 1;
+  const int64_t blocks_bound = (int64_t)num_seqs * ((max_len + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE);
+  return blocks_bound >= kStreamMinBlocksPerWg * decode_stream_wgs();
 }
 
 // Register ring depth of the decode kernel (blocks in flight per wave);
@@ -152,29 +155,22 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
   WorkspaceLayout w;
   w.prefetch = decode_prefetch(head_size);
-  w.stream = decode_use_stream(num_seqs, num_kv_heads, head_size, max_len);
-  size_t dec_o = 0, dec_ml = 0;  // fp32 elements of the decode partials
-  if (w.stream) {
-    w.stream_heads = std::min(num_kv_heads, kStreamWaves);
-    w.waves = kStreamWaves / w.stream_heads * w.stream_heads;
-    w.stream_wgs = decode_stream_wgs();
-    w.part_tokens = 0;
-    w.num_parts_max = 0;
-    const size_t rows = (size_t)w.stream_wgs * 2 * num_q_heads;  // (share, slot, head)
-    dec_o = rows * head_size;
-    dec_ml = rows * 2;
-  } else {
-    w.stream_heads = 0;
-    w.stream_wgs = 0;
-    w.waves = decode_waves(head_size, w.prefetch);
-    w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, w.waves, max_len);
-    w.num_parts_max = (max_len + w.part_tokens - 1) / w.part_tokens;
-    if (w.num_parts_max > kMaxGridZ) return false;
-    const size_t rows =
-        w.num_parts_max > 1 ? (size_t)num_seqs * w.num_parts_max * num_q_heads : 0;
-    dec_o = rows * head_size;
-    dec_ml = rows * 2;
-  }
+  // Both decode schedules' parameters; the partial results region fits
+  // either, so a per-call flag may pick one.
+  w.stream_ok = decode_stream_fits(num_seqs, num_kv_heads, head_size);
+  w.stream_default = w.stream_ok && decode_stream_default(num_seqs, max_len);
+  w.stream_heads = std::min(num_kv_heads, kStreamWaves);
+  w.stream_waves = kStreamWaves / w.stream_heads * w.stream_heads;
+  w.stream_wgs = decode_stream_wgs();
+  w.waves = decode_waves(head_size, w.prefetch);
+  w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, w.waves, max_len);
+  w.num_parts_max = (max_len + w.part_tokens - 1) / w.part_tokens;
+  if (w.num_parts_max > kMaxGridZ) return false;
+  const size_t stream_rows = w.stream_ok ? (size_t)w.stream_wgs * 2 * num_q_heads : 0;
+  const size_t part_rows =
+      w.num_parts_max > 1 ? (size_t)num_seqs * w.num_parts_max * num_q_heads : 0;
+  const size_t rows = std::max(stream_rows, part_rows);  // (share, slot, head) / (row, part, head)
+  const size_t dec_o = rows * head_size, dec_ml = rows * 2;
   w.tile_queries = prefill_tile_queries(group);
   // Each row adds at most one partial tile: sum ceil(ql/BQ) <= T/BQ + S.
   const int64_t any_bound = (int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
@@ -259,8 +255,12 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
                   int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
                   size_t workspace_bytes, uint32_t flags, void* stream) {
   g_last_error.clear();
-  if (flags & ~(uint32_t)PA_FORWARD_SHARED_BLOCKS)
+  const uint32_t known =
+      PA_FORWARD_SHARED_BLOCKS | PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED;
+  if (flags & ~known)
     return fail(PA_ERR_UNSUPPORTED, "pa_forward_ex: unknown flags 0x%x", flags);
+  if ((flags & PA_FORWARD_DECODE_EVEN_SHARES) && (flags & PA_FORWARD_DECODE_PARTITIONED))
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_ex: both decode schedule flags set");
   if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
     return fail(PA_ERR_SHAPE, "pa_forward: a size is out of range (T=%d S=%d Hq=%d Hkv=%d D=%d "
@@ -333,13 +333,15 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
     if (e != hipSuccess) return hip_fail(e, "pa_forward prefill launch");
   }
   pa::DecodePlan dp;
-  dp.stream = w.stream;
+  dp.stream = (flags & PA_FORWARD_DECODE_EVEN_SHARES)  ? w.stream_ok
+              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
+                                                        : w.stream_default;
   dp.stream_wgs = w.stream_wgs;
   dp.stream_heads = w.stream_heads;
   dp.part_tokens = w.part_tokens;
   dp.num_parts_max = w.num_parts_max;
   dp.prefetch = w.prefetch;
-  dp.waves = w.waves;
+  dp.waves = dp.stream ? w.stream_waves : w.waves;
   dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);

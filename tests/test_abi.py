@@ -95,7 +95,12 @@ def test_forward_rejects_bad_arguments(lib):
     assert fw(lib, T=0) == 0              # empty batch: no launch
     # unknown option flags are rejected before anything else happens
     assert lib.pa_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 8, 2, 32, 4, 64, 16,
+                             4, 64, 0, 0, FAKE, 1 << 30, 8, None) == -3
+    assert "unknown flags" in pa.last_error()
+    # both decode schedules at once
+    assert lib.pa_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 8, 2, 32, 4, 64, 16,
                              4, 64, 0, 0, FAKE, 1 << 30, 6, None) == -3
+    assert "schedule" in pa.last_error()
 
 
 def test_validate_rejects_null_before_touching_the_device(lib):
@@ -122,8 +127,9 @@ def test_workspace_sizes_for_the_named_workloads(lib, i):
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define PA_BLOCK_SIZE (\d+)", text).group(1)) == pa.BLOCK_SIZE
-    assert int(re.search(r"#define PA_FORWARD_SHARED_BLOCKS (\d+)u", text).group(1)) == \
-        pa.FORWARD_SHARED_BLOCKS
+    for name in ("SHARED_BLOCKS", "DECODE_EVEN_SHARES", "DECODE_PARTITIONED"):
+        assert int(re.search(rf"#define PA_FORWARD_{name} (\d+)u", text).group(1)) == \
+            getattr(pa, "FORWARD_" + name)
     m = re.search(r"#define PA_WORKSPACE_COUNTER_BYTES \((\d+)u \* (\d+)u\)", text)
     assert int(m.group(1)) * int(m.group(2)) == pa.WORKSPACE_COUNTER_BYTES
 

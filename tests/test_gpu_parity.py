@@ -124,20 +124,22 @@ def test_tiny_prefill_all_rows(hints):
     assert_close(out.cpu()[rows], want, "tiny")
 
 
-def test_decode_workload_all_rows():
+@pytest.mark.parametrize("schedule", [None, "even", "partitioned"])
+def test_decode_workload_all_rows(schedule):
     spec = wl.config(2)
-    banner("forward workload 2 (decode, 64 rows)")
+    banner(f"forward workload 2 (decode, 64 rows), schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case)
+    out = write_and_forward(case, decode_schedule=schedule)
     rows, want = oracle_rows(case, list(range(spec.num_seqs)))
     assert_close(out.cpu()[rows], want, "decode")
 
 
-def test_mixed_workload_sampled_rows():
+@pytest.mark.parametrize("schedule", [None, "partitioned"])
+def test_mixed_workload_sampled_rows(schedule):
     spec = wl.config(3)
-    banner("forward workload 3 (mixed 8192-token step), sampled rows")
+    banner(f"forward workload 3 (mixed 8192-token step), sampled rows, schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case).cpu()
+    out = write_and_forward(case, decode_schedule=schedule).cpu()
     lens = spec.seq_lens
     dec = sorted(range(256), key=lambda s: lens[s])
     dec_pick = sorted(set(dec[:4] + dec[-4:] + random.Random(3).sample(range(256), 12)))
@@ -149,11 +151,12 @@ def test_mixed_workload_sampled_rows():
     assert_close(out[rows], want, "mixed/prefill rows")
 
 
-def test_long_decode_sampled_rows():
+@pytest.mark.parametrize("schedule", [None, "partitioned"])
+def test_long_decode_sampled_rows(schedule):
     spec = wl.config(4)
-    banner("forward workload 4 (16 x 32768 decode), 3 rows")
+    banner(f"forward workload 4 (16 x 32768 decode), 3 rows, schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case).cpu()
+    out = write_and_forward(case, decode_schedule=schedule).cpu()
     rows, want = oracle_rows(case, [0, 7, 15])
     assert_close(out[rows], want, "long decode")
 
@@ -236,14 +239,15 @@ DECODE_SCHEDULE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("schedule", [None, "even", "partitioned"])
 @pytest.mark.parametrize("name,hq,hkv,d,rows", DECODE_SCHEDULE_CASES,
                          ids=[c[0] for c in DECODE_SCHEDULE_CASES])
-def test_decode_schedules(name, hq, hkv, d, rows):
+def test_decode_schedules(name, hq, hkv, d, rows, schedule):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=60 + len(rows) % 97)
-    banner(f"decode schedule {name}: S={spec.num_seqs} Hq={hq} Hkv={hkv} D={d}")
+    banner(f"decode schedule {name} ({schedule}): S={spec.num_seqs} Hq={hq} Hkv={hkv} D={d}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case)
-    out2 = write_and_forward(case).clone()
+    out = write_and_forward(case, decode_schedule=schedule)
+    out2 = write_and_forward(case, decode_schedule=schedule).clone()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
     seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
     if len(seqs) > 64:
