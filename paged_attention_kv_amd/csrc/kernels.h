@@ -60,7 +60,8 @@ size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seq
 
 // Prefill rows (q_len > 1): a planner writes the tile list, then the tiles run.
 struct PrefillPlan {
-  int32_t tile_queries;  // query tokens per tile
+  int32_t tile_queries;        // query tokens per list-A tile
+  int32_t split_tile_queries;  // query tokens per list-B tile
   int32_t bound_a;       // entries of list A (tiles seeing many keys)
   int32_t bound_b;       // entries of list B (tiles seeing few keys)
   int32_t* tiles_a;      // [bound_a][2] (sequence, first query row) or -1
@@ -68,8 +69,10 @@ struct PrefillPlan {
   int32_t* counts;       // [2] tiles the planner put in lists A and B
 };
 hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
-// Query tokens per prefill tile for a given group size (128 MFMA rows / G).
+// Query tokens per prefill tile for a given group size (MFMA rows / G), for
+// tiles whose rows see many keys (list A) and few (list B).
 int32_t prefill_tile_queries(int32_t group);
+int32_t prefill_split_tile_queries(int32_t group);
 // Upper bound on list-B tiles per row.
 int32_t prefill_split_tiles_per_row(int32_t group);
 

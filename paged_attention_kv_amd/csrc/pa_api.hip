@@ -172,11 +172,11 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   const size_t rows = std::max(stream_rows, part_rows);  // (share, slot, head) / (row, part, head)
   const size_t dec_o = rows * head_size, dec_ml = rows * 2;
   w.tile_queries = prefill_tile_queries(group);
-  // Each row adds at most one partial tile: sum ceil(ql/BQ) <= T/BQ + S.
-  const int64_t any_bound = (int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
-  w.bound_a = (int32_t)any_bound;
-  w.bound_b = (int32_t)std::min<int64_t>(
-      any_bound, (int64_t)num_seqs * prefill_split_tiles_per_row(group));
+  const int32_t bq_b = prefill_split_tile_queries(group);
+  // Each row adds at most one partial tile per list: sum ceil(ql/BQ) <= T/BQ + S.
+  w.bound_a = (int32_t)((int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs);
+  w.bound_b = (int32_t)std::min<int64_t>((int64_t)(num_tokens + bq_b - 1) / bq_b + num_seqs,
+                                         (int64_t)num_seqs * prefill_split_tiles_per_row(group));
   w.off_ctr = 0;
   w.off_o = round_up((size_t)kCounterSlots * sizeof(int32_t), kAlign);
   w.off_ml = round_up(w.off_o + dec_o * sizeof(float), kAlign);
@@ -322,10 +322,13 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
   if (a.max_query_len > 1) {
     pa::PrefillPlan pp;
     pp.tile_queries = w.tile_queries;
-    const int64_t by_hint =
+    pp.split_tile_queries = pa::prefill_split_tile_queries(num_q_heads / num_kv_heads);
+    const int64_t by_hint_a =
         (int64_t)num_seqs * ((a.max_query_len + w.tile_queries - 1) / w.tile_queries);
-    pp.bound_a = (int32_t)std::min<int64_t>(w.bound_a, by_hint);
-    pp.bound_b = (int32_t)std::min<int64_t>(w.bound_b, by_hint);
+    const int64_t by_hint_b =
+        (int64_t)num_seqs * ((a.max_query_len + pp.split_tile_queries - 1) / pp.split_tile_queries);
+    pp.bound_a = (int32_t)std::min<int64_t>(w.bound_a, by_hint_a);
+    pp.bound_b = (int32_t)std::min<int64_t>(w.bound_b, by_hint_b);
     pp.tiles_a = (int32_t*)(ws + w.off_tiles_a);
     pp.tiles_b = (int32_t*)(ws + w.off_tiles_b);
     pp.counts = (int32_t*)(ws + w.off_counts);

@@ -11,20 +11,21 @@
 // tokens sits at position c + i and sees keys 0..c+i.
 //
 // gfx950 design: one workgroup = one (sequence, tile of query tokens, KV
-// head) with 4 waves. The tile packs the G query heads that share the KV head
-// into the MFMA M dimension: 128 rows = (128/G tokens) x (G heads), 32 rows
-// per wave, so every K/V tile staged in LDS serves all G heads. Per 64-key
-// tile each wave computes S^T = K Q^T (keys x rows) with 16x16x32 bf16 MFMAs
-// (K rows read from LDS, Q^T held in registers), applies the bottom-right
-// causal mask (only on tiles that reach past the first row's limit) and an
-// fp32 online softmax with a lazily re-referenced max, and accumulates
-// O^T += V^T P^T with 16x16x32 MFMAs whose B operand is the S^T accumulator
-// converted to bf16 in place (as hi + lo parts when the tile's rows see few
-// keys). K/V tiles are double-buffered in LDS through registers: the global
-// loads of tile t+2 are in flight while tile t computes and tile t+1 is
-// stored, with one barrier per tile. A single-workgroup planner kernel turns
-// query_start_loc into the list of tiles on the device, so the host never
-// reads lengths.
+// head) with NW waves. The tile packs the G query heads that share the KV
+// head into the MFMA M dimension: 32*NW rows = (32*NW/G tokens) x (G heads),
+// 32 rows per wave, so every K/V tile staged in LDS serves all G heads. Per
+// 64-key tile each wave computes S^T = K Q^T (keys x rows) with 16x16x32 bf16
+// MFMAs (K rows read from LDS, Q^T held in registers), applies the
+// bottom-right causal mask (only on tiles that reach past the first row's
+// limit) and an fp32 online softmax with a lazily re-referenced max, and
+// accumulates O^T += V^T P^T with 16x16x32 MFMAs whose B operand is the S^T
+// accumulator converted to bf16 in place (as hi + lo parts when the tile's
+// rows see few keys). K/V tiles move from HBM/L2 straight into a ring of NST
+// LDS stages (global_load_lds), NST-1 tiles ahead of the one being computed;
+// each tile starts with a wait for that tile's own loads (an explicit
+// vmcnt count, so the later tiles' loads stay in flight) and one barrier. A
+// single-workgroup planner kernel turns query_start_loc into the lists of
+// tiles on the device, so the host never reads lengths.
 #include <math.h>
 
 #include <algorithm>
@@ -37,8 +38,12 @@ namespace pa {
 
 namespace {
 
-constexpr int kPrefillThreads = 256;
-constexpr int kRowsPerWG = 128;
+// List A tiles (rows that see many keys): 8 waves (256 MFMA rows: each K/V
+// tile staged in LDS serves twice the rows of a 4-wave tile), two LDS stages
+// (a third measured slower). List B tiles (rows that see few keys, P kept as
+// hi + lo, which needs more registers): 4 waves (128 rows), two stages.
+constexpr int kWavesA = 8, kStagesA = 2;
+constexpr int kWavesB = 4, kStagesB = 2;
 constexpr int kKeysPerTile = 64;
 constexpr float kLazyP = 8.0f;  // log2 of the largest unnormalised weight
 constexpr int kSplitKeys = 128;  // workgroups seeing at most this many keys split P
@@ -51,7 +56,7 @@ constexpr int kPlanThreads = 1024;
 // kSplitKeys keys (they keep P as bf16 hi + lo).
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
-    int32_t tile_queries, int32_t* __restrict__ tiles_a, int32_t bound_a,
+    int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
     int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts) {
   __shared__ int32_t scan_a[kPlanThreads], scan_b[kPlanThreads];
   __shared__ int32_t carry_a, carry_b;
@@ -60,15 +65,16 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   __syncthreads();
   for (int base = 0; base < S; base += kPlanThreads) {
     const int s = base + tid;
-    int na = 0, nb = 0, ql = 0, c = 0;
+    int na = 0, nb = 0, ql = 0, c = 0, qa = 0;
     if (s < S) {
       ql = qsl[s + 1] - qsl[s];
       c = seq_lens[s] - ql;
       if (ql > 1) {
-        const int n = (ql + tile_queries - 1) / tile_queries;
-        // kv_end of tile t is c + t*BQ + min(BQ, ql - t*BQ): non-decreasing in t
-        while (nb < n && c + min((nb + 1) * tile_queries, ql) <= kSplitKeys) ++nb;
-        na = n - nb;
+        const int n = (ql + bq_b - 1) / bq_b;
+        // kv_end of B tile t is c + min((t+1)*bq_b, ql): non-decreasing in t
+        while (nb < n && c + min((nb + 1) * bq_b, ql) <= kSplitKeys) ++nb;
+        qa = min(ql, nb * bq_b);  // A tiles cover queries [qa, ql)
+        na = (ql - qa + bq_a - 1) / bq_a;
       }
     }
     scan_a[tid] = na;
@@ -88,14 +94,14 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
       const int idx = off_a + k;
       if (idx < bound_a) {
         tiles_a[2 * idx] = s;
-        tiles_a[2 * idx + 1] = (nb + na - 1 - k) * tile_queries;
+        tiles_a[2 * idx + 1] = qa + (na - 1 - k) * bq_a;
       }
     }
     for (int k = 0; k < nb; ++k) {
       const int idx = off_b + k;
       if (idx < bound_b) {
         tiles_b[2 * idx] = s;
-        tiles_b[2 * idx + 1] = k * tile_queries;
+        tiles_b[2 * idx + 1] = k * bq_b;
       }
     }
     __syncthreads();
@@ -119,35 +125,60 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
   }
 }
 
-// LDS chunk swizzles of the K and V tiles (see the kernel).
-__device__ __forceinline__ int swz_k(int r) { return r & 7; }
-__device__ __forceinline__ int swz_v(int r) { return 2 * (r & 3); }
+// Waits until at most N vector-memory operations of this wave are in flight
+// (its loads into LDS of older tiles have landed; the N most recent stay in
+// flight), then joins the workgroup barrier. One asm statement with a memory
+// clobber, so the compiler neither adds a full drain nor moves LDS accesses
+// across it.
+template <int N>
+__device__ __forceinline__ void wait_loads_then_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// Waits for this wave's LDS writes, then joins the workgroup barrier.
+__device__ __forceinline__ void lds_writes_then_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS chunk swizzles of the K and V tiles: 16-byte chunk c of row r sits at
+// chunk c ^ swz(r). gfx950's LDS serves 256 bytes per cycle (64 banks): a
+// 16-byte read takes 16 lanes per cycle, an 8-byte transpose read 32. The K
+// row reads (lane: row hl of 16, one logical chunk) and the V transpose reads
+// (lanes: 8 rows x 2 chunks x 2 halves) then each hit 16 / 32 distinct bank
+// slots. Rows are 2*D bytes: at D = 64 two rows share the 256 bytes, so the
+// swizzle keys on r / 2.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
 template <int D, int G, bool SPLIT>
-__global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_kernel(
+__global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefill_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, float scale_log2, int32_t Hq, int32_t Hkv,
     int32_t MB, int32_t tile_bound) {
-  constexpr int BQ = kRowsPerWG / G;          // query tokens per tile
+  constexpr int NW = SPLIT ? kWavesB : kWavesA;   // waves
+  constexpr int NST = SPLIT ? kStagesB : kStagesA;  // LDS stages
+  constexpr int BQ = 32 * NW / G;             // query tokens per tile
   constexpr int BN = kKeysPerTile;            // keys per iteration
   constexpr int RB = D * 2;                   // bytes of one K or V row (unpadded)
   constexpr int KC = D / 32;                  // QK MFMAs per 16x16 S tile
   constexpr int DT = D / 16;                  // PV output tiles along d
   constexpr int NS = BN / 16;                 // 16-key sub-tiles per tile
   constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
-  constexpr int NDMA = BN * RB / 1024 / 4;    // 1 KiB load-to-LDS ops per wave per tile
-  static_assert(NDMA * 4 * 1024 == BN * RB, "tile must split evenly");
+  constexpr int NDMA = BN * RB / 1024 / NW;   // 1 KiB load-to-LDS ops per wave per tile (K; V alike)
+  static_assert(NDMA * NW * 1024 == BN * RB, "tile must split evenly");
+  static_assert(NST == 2 || NST == 3, "stage count");
 
-  // Two stages (the tile being computed and the one being filled), rows
+  // NST stages (the tile being computed and the ones being filled), rows
   // unpadded; 16-byte chunk c of row r sits at chunk c ^ swz(r) so that both
   // the row reads of the QK operand (8 rows per phase, K) and the transpose
   // reads of the PV operand (4 rows per 16-lane block, V) are bank-conflict
   // free.
-  __shared__ __attribute__((aligned(1024))) uint8_t ks[2][BN * RB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs[2][BN * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks[NST][BN * RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs[NST][BN * RB];
 
   // One (sequence, query tile, KV head) task.
   auto run_tile = [&](const int s, const int q0, const int g) {
@@ -164,7 +195,7 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: scalar table reads
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int64_t kv_row = (int64_t)Hkv * D;
@@ -203,30 +234,31 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   const int32_t* table = block_table + (int64_t)s * MB;
   const int last_blk = (kv_end - 1) / kBlock;  // last block any row reads
   constexpr int kTileBlocks = BN / kBlock;     // 16-token blocks per key tile
-  // Block ids of key tile kt: lane b < kTileBlocks holds entry kt*4 + b
-  // (clamped to the last block read), fetched one iteration ahead.
-  auto tile_ids = [&](int kt) __attribute__((always_inline)) {
-    return lane < kTileBlocks ? table[min(kt * kTileBlocks + lane, last_blk)] : 0;
+  // Load op j of wave w fills LDS bytes (j*NW + w)*1024 .. +1024 of a stage:
+  // rows of one 16-key block (block kb(j) of the tile), lane l the 16 bytes
+  // at l*16. Its table entry is wave-uniform (a scalar load), read one tile
+  // ahead and clamped to the last block any row reads.
+  auto kb = [&](int j) { return ((j * NW + w) * 1024 / RB) / kBlock; };
+  auto tile_ids = [&](int kt, int (&ids)[NDMA]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) ids[j] = table[min(kt * kTileBlocks + kb(j), last_blk)];
   };
-  // Tile kt straight from HBM/L2 into LDS stage `stage`: load op j of wave w
-  // fills LDS bytes (j*4 + w)*1024 .. +1024, lane l the 16 bytes at l*16,
-  // i.e. row r, physical chunk pc; it fetches logical chunk pc ^ swz(r) of
-  // key kt*64 + r. The rows of one op lie in one 16-key block (wave-uniform
-  // table id).
-  auto dma_tile = [&](int kt, int stage, int ids) __attribute__((always_inline)) {
+  // Tile kt straight from HBM/L2 into LDS stage `stage`: lane l of op j
+  // covers row r, physical chunk pc, and fetches logical chunk pc ^ swz(r)
+  // of key kt*64 + r.
+  auto dma_tile = [&](int stage, const int (&ids)[NDMA]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int p = (j * 4 + w) * 1024 + lane * 16;
+      const int p = (j * NW + w) * 1024 + lane * 16;
       const int r = p / RB;
       const int pc = (p % RB) / 16;
-      const int64_t blk = __builtin_amdgcn_readlane(ids, ((j * 4 + w) * 1024 / RB) / kBlock);
-      const int64_t row = (blk * kBlock + r % kBlock) * kv_row + (int64_t)g * D;
+      const int64_t row = ((int64_t)ids[j] * kBlock + r % kBlock) * kv_row + (int64_t)g * D;
       __builtin_amdgcn_global_load_lds(
-          (const void*)(k_cache + row + (pc ^ swz_k(r)) * 8),
-          (__attribute__((address_space(3))) void*)(&ks[stage][(j * 4 + w) * 1024]), 16, 0, 0);
+          (const void*)(k_cache + row + (pc ^ swz_k<D>(r)) * 8),
+          (__attribute__((address_space(3))) void*)(&ks[stage][(j * NW + w) * 1024]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
-          (const void*)(v_cache + row + (pc ^ swz_v(r)) * 8),
-          (__attribute__((address_space(3))) void*)(&vs[stage][(j * 4 + w) * 1024]), 16, 0, 0);
+          (const void*)(v_cache + row + (pc ^ swz_v<D>(r)) * 8),
+          (__attribute__((address_space(3))) void*)(&vs[stage][(j * NW + w) * 1024]), 16, 0, 0);
     }
   };
   // Rows of tile kt at or past kv_end came from a clamped or partly used
@@ -235,26 +267,26 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   auto zero_tail = [&](int kt, int stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int p = (j * 4 + w) * 1024 + lane * 16;
+      const int p = (j * NW + w) * 1024 + lane * 16;
       if (kt * BN + p / RB >= kv_end) *(u32x4*)(&vs[stage][p]) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
   // Per-lane LDS byte offsets of the operand reads, so that the rest of each
-  // address is a compile-time immediate.
-  // K (QK A operand): lane reads row n*16 + hl, logical chunk 4i + grp, which
-  // sits at chunk (4i + grp) ^ swz_k(hl) = 8*(i/2) + ((4*(i%2) + grp) ^ (hl%8)).
-  int koff[2];
+  // address is a compile-time immediate (the swizzles depend on a row only
+  // through its low bits, which the 16- and 32-row steps leave alone).
+  // K (QK A operand): lane reads row n*16 + hl, logical chunk 4i + grp.
+  int koff[KC];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) koff[b] = hl * RB + (((4 * b + grp) ^ swz_k(hl)) * 16);
+  for (int i = 0; i < KC; ++i) koff[i] = hl * RB + (((4 * i + grp) ^ swz_k<D>(hl)) * 16);
   // V (PV A operand, transpose reads): lane reads row kp*32 + 4*grp + hl/4
-  // (and 16 rows on), 8 bytes at half (hl%2) of logical chunk 2*mi + (hl%4)/2,
-  // which sits at chunk 8*(mi/4) + ((2*(mi%4) + (hl%4)/2) ^ swz_v(hl/4)).
-  int voff[4];
+  // (and 16 rows on), 8 bytes at half (hl%2) of logical chunk 2*mi + (hl%4)/2.
+  int voff[DT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    voff[j] = (4 * grp + hl / 4) * RB + (hl & 1) * 8 +
-              (((2 * j + (hl % 4) / 2) ^ swz_v(hl / 4)) * 16);
+  for (int mi = 0; mi < DT; ++mi) {
+    const int r0 = 4 * grp + hl / 4;
+    voff[mi] = r0 * RB + (hl & 1) * 8 + (((2 * mi + (hl % 4) / 2) ^ swz_v<D>(r0)) * 16);
+  }
 
   // One 64-key tile: S^T = K Q^T, masked online softmax, O^T += V^T P^T.
   // split: P enters PV as bf16 hi + lo parts (rows with few visible keys).
@@ -272,7 +304,7 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
     for (int n = 0; n < NS; ++n) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + n * 16 * RB + koff[i & 1] + (i >> 1) * 128));
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + n * 16 * RB + koff[i]));
         st[0][n] = mfma_16x16x32(a, qv[0][i], st[0][n]);
         st[1][n] = mfma_16x16x32(a, qv[1][i], st[1][n]);
       }
@@ -356,7 +388,7 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
       const uint8_t* vrow0 = vst + kp * 32 * RB;
 #pragma unroll
       for (int mi = 0; mi < DT; ++mi) {
-        const uint8_t* va = vrow0 + voff[mi & 3] + (mi >> 2) * 128;
+        const uint8_t* va = vrow0 + voff[mi];
         const i16x4 a0 = lds_read_tr16((const uint16_t*)va);
         const i16x4 a1 = lds_read_tr16((const uint16_t*)(va + 16 * RB));
         const bf16x8 av = __builtin_bit_cast(
@@ -377,30 +409,43 @@ __global__ __launch_bounds__(kPrefillThreads, SPLIT ? 1 : 2) void prefill_tile_k
   };
 
 
-  // One key tile; the loop is unrolled by two so that the LDS stage of each
-  // half is a compile-time constant (LDS offsets become immediates).
-  int ids_next = tile_ids(1);
-  auto step = [&](int kt, int stage) __attribute__((always_inline)) {
-    // This wave's loads into `stage` are complete (the barrier's release
-    // waits for all of them), every wave's are once all have arrived, and
-    // every wave is done reading tile kt-1 from the other stage.
-    __syncthreads();
+  // Tiles 0 .. NST-2 are issued up front; at tile kt the loads of tiles
+  // kt .. kt+NST-2 are in flight. Each step waits for tile kt's loads only
+  // (2*NDMA operations per later tile in flight stay outstanding), joins the
+  // barrier (every wave's part of tile kt has landed, and every wave is done
+  // reading tile kt-1, whose stage the next issue overwrites), then issues
+  // tile kt+NST-1 and computes tile kt.
+  constexpr int kOps = 2 * NDMA;  // vector-memory operations per tile per wave
+  int ids[NDMA];
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u) {
+    if (u < ntiles) {
+      tile_ids(u, ids);
+      dma_tile(u, ids);
+    }
+  }
+  tile_ids(NST - 1, ids);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int stage = kt % NST;
+    const int later = min(NST - 2, ntiles - 1 - kt);  // tiles issued after kt
+    if (NST == 3 && later == 1) wait_loads_then_barrier<kOps>();
+    else wait_loads_then_barrier<0>();
     if ((kt + 1) * BN > kv_end) {
       zero_tail(kt, stage);
-      __syncthreads();
+      lds_writes_then_barrier();
     }
-    if (kt + 1 < ntiles) {
-      dma_tile(kt + 1, stage ^ 1, ids_next);
-      ids_next = tile_ids(kt + 2);
-    }
+    if (kt + NST - 1 < ntiles) dma_tile((kt + NST - 1) % NST, ids);
     const bool masked = (kt + 1) * BN - 1 > first_lim;
     // Tiles whose rows see at most kSplitKeys keys (SPLIT) keep P to about
     // 2^-17 (hi + lo): few weights carry each output there, and bf16
     // rounding of P would show in it.
     compute_tile(kt, stage, masked, std::integral_constant<bool, SPLIT>{});
-  };
-  dma_tile(0, 0, tile_ids(0));
-  for (int kt = 0; kt < ntiles; ++kt) step(kt, kt & 1);
+    // The next tile's table entries: scalar loads share a wait counter with
+    // LDS reads, so they are issued after this tile's last LDS read (and
+    // kept there) and land while the next step waits for its tile.
+    __builtin_amdgcn_sched_barrier(0);
+    tile_ids(kt + NST, ids);
+  }
 
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -451,7 +496,7 @@ hipError_t launch_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t 
     if (grid > INT32_MAX) return hipErrorInvalidValue;
     profile_begin(PA_KERNEL_PREFILL, stream);
     hipLaunchKernelGGL((prefill_tile_kernel<D, G, false>), dim3((unsigned)grid),
-                       dim3(kPrefillThreads), 0, stream, (const uint16_t*)a.q,
+                       dim3(kWavesA * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_table,
                        a.seq_lens, a.query_start_loc, (uint16_t*)a.out, p.tiles_a, p.counts,
                        scale_log2, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
@@ -465,7 +510,7 @@ hipError_t launch_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t 
         std::min<int64_t>((int64_t)p.bound_b * a.num_kv_heads, kSplitGridMax);
     profile_begin(PA_KERNEL_PREFILL_SHORT, stream);
     hipLaunchKernelGGL((prefill_tile_kernel<D, G, true>), dim3((unsigned)grid),
-                       dim3(kPrefillThreads), 0, stream, (const uint16_t*)a.q,
+                       dim3(kWavesB * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_table,
                        a.seq_lens, a.query_start_loc, (uint16_t*)a.out, p.tiles_b,
                        p.counts + 1, scale_log2, a.num_q_heads, a.num_kv_heads,
@@ -490,10 +535,11 @@ hipError_t launch_tiles_d(const ForwardArgs& a, const PrefillPlan& p, hipStream_
 
 }  // namespace
 
-int32_t prefill_tile_queries(int32_t group) { return kRowsPerWG / group; }
+int32_t prefill_tile_queries(int32_t group) { return 32 * kWavesA / group; }
+int32_t prefill_split_tile_queries(int32_t group) { return 32 * kWavesB / group; }
 
 int32_t prefill_split_tiles_per_row(int32_t group) {
-  const int32_t bq = kRowsPerWG / group;
+  const int32_t bq = 32 * kWavesB / group;
   return (kSplitKeys + bq - 1) / bq;
 }
 
@@ -501,7 +547,8 @@ hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_
   if (p.bound_a <= 0 && p.bound_b <= 0) return hipSuccess;
   profile_begin(PA_KERNEL_PLAN, stream);
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
-                     a.query_start_loc, a.seq_lens, a.num_seqs, p.tile_queries, p.tiles_a,
+                     a.query_start_loc, a.seq_lens, a.num_seqs, p.tile_queries,
+                     p.split_tile_queries, p.tiles_a,
                      p.bound_a, p.tiles_b, p.bound_b, p.counts);
   profile_end(PA_KERNEL_PLAN, stream);
   hipError_t e = hipGetLastError();
