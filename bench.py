@@ -1,9 +1,11 @@
 """Benchmark of the paged-attention hot path on one MI355X.
 
 One step = the whole hot path over one batch: the KV-cache write of the
-step's new tokens (pa_cache_write) followed by paged attention of the
-flattened batch (pa_forward). Inputs are synthetic, seeded, and resident in
-HBM before the timed region starts.
+step's new tokens and paged attention of the flattened batch, through
+pa_write_and_forward (one launch for a batch of decode rows on the
+partitioned schedule; a write launch and the forward launches otherwise).
+Inputs are synthetic, seeded, and resident in HBM before the timed region
+starts.
 
 Headline (one JSON line on stdout):
   * value: decode GB/s on the decode workload (64 sequences x 1 query token,
@@ -14,9 +16,9 @@ Headline (one JSON line on stdout):
     Cache cannot hold a step's KV.
   * mixed_step: tokens/s of the 8192-token mixed chunked-prefill step (256
     decode rows + 4 x 1984-token chunks, 32 q / 8 kv heads, D 128).
-  * roofline: the decode kernel's algorithmic bytes per launch over its
-    average launch duration (HIP events on the launch stream), against
-    8 TB/s.
+  * roofline: the decode kernel's algorithmic bytes per launch (with the
+    KV write when the launch does it) over its average launch duration (HIP
+    events on the launch stream), against 8 TB/s.
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only decode|mixed]
@@ -149,9 +151,9 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int):
 
     def step(i):
         st = inp.sets[i % inp.rotations]
-        pa.cache_write(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache)
-        pa.forward(st["q"], inp.k_cache, inp.v_cache, st["block_table"], inp.seq_lens, inp.qsl,
-                   spec.scale, out=st["out"], **inp.hints)
+        pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
+                             st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
+                             out=st["out"], **inp.hints)
 
     for i in range(warmup):
         step(i)
@@ -288,9 +290,11 @@ def main(argv=None):
         b_step = b_attn + write_bytes(spec)
         gbs = b_step / (ms_step * 1e-3) / 1e9
         ms_dec = kmean["decode"]
+        fused = "cache_write" not in kcount  # the decode launch also wrote the new tokens
+        b_dec = b_step if fused else b_attn
         result["decode"] = dict(ms_step=ms_step, gbs=gbs, ms_fwd=ms_fwd, ms_decode_kernel=ms_dec,
-                                kernel_gbs=b_attn / (ms_dec * 1e-3) / 1e9, bytes_step=b_step,
-                                bytes_fwd=b_attn, rotations=inp.rotations,
+                                kernel_gbs=b_dec / (ms_dec * 1e-3) / 1e9, bytes_step=b_step,
+                                bytes_fwd=b_dec, fused=fused, rotations=inp.rotations,
                                 kernels={k: round(v * 1e3, 3) for k, v in kmean.items()})
         del inp
         torch.cuda.empty_cache()
@@ -361,10 +365,11 @@ def main(argv=None):
             "tokens": 64, "kv_bytes_per_step": d["bytes_step"],
             "block_table_rotations": d["rotations"],
             "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
-        line["roofline"] = {"bound": "hbm", "kernel": "decode_kernel<64, 2, true>",
+        kname = "decode_kernel<64, 2, true, %s>" % ("true" if d["fused"] else "false")
+        line["roofline"] = {"bound": "hbm", "kernel": kname,
                             "achieved": round(d["kernel_gbs"], 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("decode_kernel<64, 2, true>", "decode ("),
+                            "traffic": measured_traffic(kname, "decode ("),
                             "avg_launch_us": round(d["ms_decode_kernel"] * 1e3, 3),
                             "algorithmic_bytes_per_launch": d["bytes_fwd"],
                             "forward_kernels_us_per_step": round(d["ms_fwd"] * 1e3, 3),

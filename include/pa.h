@@ -187,6 +187,40 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
                   size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * The step's KV write and its attention in one call: the same results as
+ * pa_cache_write(k, v, slot_mapping, k_cache, v_cache, num_tokens,
+ * num_kv_heads, head_size, num_blocks, block_size, stream) followed by
+ * pa_forward_ex(q, k_cache, v_cache, ..., flags, stream) (the write feeds the
+ * forward pass, section "Prefix Caching"; both per section "Run forward
+ * pass"). When max_query_len_hint == 1 (every row is a decode row) and the
+ * decode rows take the partitioned schedule, a single launch does both: each
+ * row's workgroups write its new token into the caches and read that token
+ * from k and v rather than from the slot being written. Otherwise the write
+ * is a launch of its own ahead of the forward launches.
+ *
+ *   k, v, slot_mapping   as for pa_cache_write (k, v: bf16 [num_tokens,
+ *                        num_kv_heads, head_size]; slot_mapping int64
+ *                        [num_tokens], < 0 skips a token)
+ *   everything else      as for pa_forward_ex; k_cache, v_cache are written
+ *
+ * Caller contract of the single launch (the pages' slot mapping): token
+ * qsl[s] of decode row s is its position seq_lens[s] - 1, slot_mapping of it
+ * (when >= 0) is that position's slot in row s's blocks, and no other row of
+ * the call reads a slot being written (a block being appended to is not
+ * shared). A token whose slot is < 0 is not written and is read from the
+ * cache, as in the two-call sequence. Errors as for pa_cache_write and
+ * pa_forward_ex; on an error nothing is launched.
+ */
+int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mapping,
+                         void* k_cache, void* v_cache, const void* q, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* query_start_loc, float scale,
+                         void* out, int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                         int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                         size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
  * Synchronous check of the device-resident metadata that the hot path
  * trusts (for tests and debugging; copies to the host and waits on
  * `stream`). Checks: query_start_loc starts at 0, never decreases and ends at

@@ -16,7 +16,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["cache_write", "forward", "forward_workspace_bytes", "validate_inputs",
+__all__ = ["cache_write", "forward", "write_and_forward", "forward_workspace_bytes",
+           "validate_inputs",
            "kv_block_bytes", "last_error", "version", "library_path", "load_library",
            "profile_begin", "profile_end", "PaError", "BLOCK_SIZE", "KERNEL_CLASSES"]
 
@@ -49,6 +50,9 @@ SIGNATURES = {
     "pa_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
                                      _I32, _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ,
                                      ctypes.c_uint32, _P]),
+    "pa_write_and_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                            _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
+                                            _I32, _I32, _P, _SZ, ctypes.c_uint32, _P]),
     "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                           _I32, _I32, _P]),
     "pa_profile_begin": (ctypes.c_int, []),
@@ -173,22 +177,10 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-            block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
-            scale: float, out: Optional[torch.Tensor] = None,
-            max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
-            workspace: Optional[torch.Tensor] = None,
-            shared_blocks: bool = False,
-            decode_schedule: Optional[str] = None) -> torch.Tensor:
-    """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
-    paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
-    ``max_seq_len`` are optional host upper bounds that shrink the launch
-    grids; ``workspace`` (uint8, on the device, its first
-    ``WORKSPACE_COUNTER_BYTES`` zero before its first use) is taken from a
-    per-device cache when omitted. ``shared_blocks`` tells the library that
-    some blocks appear in several rows' tables (prefix caching); results are
-    the same either way. ``decode_schedule`` ("even" or "partitioned")
-    forces the decode rows' schedule; by default the library picks."""
+def _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out,
+                  max_query_len, max_seq_len, workspace, shared_blocks, decode_schedule):
+    """Checks and marshals the arguments shared by pa_forward_ex and
+    pa_write_and_forward: returns (q .. out pointers and sizes .. stream), out."""
     lib = load_library()
     _dev_tensor("q", q, torch.bfloat16, 3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -219,12 +211,61 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         workspace = _workspace(q.device, need)
     elif workspace.device != q.device:
         raise ValueError("workspace must be on q's device")
-    _check(lib.pa_forward_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                             block_table.data_ptr(), seq_lens.data_ptr(),
-                             query_start_loc.data_ptr(), float(scale), out.data_ptr(), T, S, Hq,
-                             Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
-                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             flags, _stream(q)))
+    tail = (block_table.data_ptr(), seq_lens.data_ptr(), query_start_loc.data_ptr(), float(scale),
+            out.data_ptr(), T, S, Hq, Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), flags, _stream(q))
+    return tail, out
+
+
+def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+            block_table: torch.Tensor, seq_lens: torch.Tensor, query_start_loc: torch.Tensor,
+            scale: float, out: Optional[torch.Tensor] = None,
+            max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
+            workspace: Optional[torch.Tensor] = None,
+            shared_blocks: bool = False,
+            decode_schedule: Optional[str] = None) -> torch.Tensor:
+    """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
+    paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
+    ``max_seq_len`` are optional host upper bounds that shrink the launch
+    grids; ``workspace`` (uint8, on the device, its first
+    ``WORKSPACE_COUNTER_BYTES`` zero before its first use) is taken from a
+    per-device cache when omitted. ``shared_blocks`` tells the library that
+    some blocks appear in several rows' tables (prefix caching); results are
+    the same either way. ``decode_schedule`` ("even" or "partitioned")
+    forces the decode rows' schedule; by default the library picks."""
+    tail, out = _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                              out, max_query_len, max_seq_len, workspace, shared_blocks,
+                              decode_schedule)
+    _check(load_library().pa_forward_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                         *tail))
+    return out
+
+
+def write_and_forward(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor,
+                      block_table: torch.Tensor, seq_lens: torch.Tensor,
+                      query_start_loc: torch.Tensor, scale: float,
+                      out: Optional[torch.Tensor] = None,
+                      max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      shared_blocks: bool = False,
+                      decode_schedule: Optional[str] = None) -> torch.Tensor:
+    """``cache_write`` then ``forward`` in one call (pa_write_and_forward):
+    with ``max_query_len=1`` (decode rows only) one launch writes the new
+    tokens and attends. Returns ``out``."""
+    for n, t in (("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("k, v, slot_mapping and q disagree in token count")
+    if tuple(k.shape[1:]) != tuple(k_cache.shape[2:]):
+        raise ValueError("k must be [T, Hkv, D] matching the caches")
+    tail, out = _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                              out, max_query_len, max_seq_len, workspace, shared_blocks,
+                              decode_schedule)
+    _check(load_library().pa_write_and_forward(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                               k_cache.data_ptr(), v_cache.data_ptr(),
+                                               q.data_ptr(), *tail))
     return out
 
 

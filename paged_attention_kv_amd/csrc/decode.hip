@@ -124,17 +124,27 @@ __device__ __forceinline__ void load_q(bf16x8 (&qv)[D / 32], const uint16_t* __r
   }
 }
 
+// Where a kernel also writes the step's new tokens into the cache (the fused
+// write), it reads the row's newest token from the step's own k and v, not
+// from the cache slot being written in the same launch.
+struct NewToken {
+  int tok;                          // its position in the row (-1: none)
+  const uint16_t* __restrict__ k;   // its K of this KV head (D elements)
+  const uint16_t* __restrict__ v;   // its V of this KV head
+};
+
 // Streams nk (1..64) blocks of one KV head into acc: block k's id sits in lane
 // k of `ids`, its first token is tok0 + k * tok_step, and tokens >= tok_end
 // are masked (their V rows zeroed). kbase / vbase point at the head's slice
 // of block 0 (kbase already offset to the lane's K row and chunk); vl is the
-// wave's LDS slice.
-template <int D, int NBUF, bool kStreamV>
+// wave's LDS slice. With kNew, token nt.tok is read from nt.k / nt.v.
+template <int D, int NBUF, bool kStreamV, bool kNew = false>
 __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv)[D / 32], int ids,
                                               int nk, int tok0, int tok_step, int tok_end,
                                               const uint16_t* __restrict__ kbase,
                                               const uint16_t* __restrict__ vbase, int64_t kv_row,
-                                              uint16_t* vl, float scale_log2, int lane) {
+                                              uint16_t* vl, float scale_log2, int lane,
+                                              NewToken nt = NewToken{-1, nullptr, nullptr}) {
   using Sh = DecodeShape<D>;
   const int hl = lane & 15;
   const int grp = lane >> 4;
@@ -145,9 +155,13 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
   // measured faster that way. K keeps plain loads: two of its loads cover the
   // two halves of one 128-byte line, which streaming loads re-fetch.
   auto load_block = [&](int k, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
-    const int64_t blk = __builtin_amdgcn_readlane(ids, min(k, nk - 1));
+    const int kc = min(k, nk - 1);
+    const int64_t blk = __builtin_amdgcn_readlane(ids, kc);
     const int64_t boff = blk * kBlock * kv_row;
     const u32x4* kp = (const u32x4*)(kbase + boff);
+    if constexpr (kNew) {
+      if (tok0 + kc * tok_step + hl == nt.tok) kp = (const u32x4*)(nt.k + 8 * grp);
+    }
 #pragma unroll
     for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = kp[4 * i];
 #pragma unroll
@@ -156,6 +170,9 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
       const int row = idx / (D / 8);
       const int col8 = idx % (D / 8);
       const u32x4* vp = (const u32x4*)(vbase + boff + row * kv_row + col8 * 8);
+      if constexpr (kNew) {
+        if (tok0 + kc * tok_step + row == nt.tok) vp = (const u32x4*)(nt.v + col8 * 8);
+      }
       vv[c] = kStreamV ? __builtin_nontemporal_load(vp) : *vp;
     }
   };
@@ -502,14 +519,20 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
 // Partitioned schedule
 // ---------------------------------------------------------------------------
 
-template <int D, int NBUF, bool kStreamV>
+// kWrite (fused write): the batch is decode rows only and this launch also
+// writes each row's new token (token qsl[s], at position seq_lens[s] - 1)
+// into the caches at slot_mapping[qsl[s]]: the workgroup of the row's last
+// partition writes its KV head's slice, and every workgroup reads that token
+// from knew / vnew.
+template <int D, int NBUF, bool kStreamV, bool kWrite>
 __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     float scale_log2, int32_t Hq, int32_t Hkv, int32_t G, int32_t MB, int32_t part_tokens,
-    int32_t num_parts_max) {
+    int32_t num_parts_max, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
+    const int64_t* __restrict__ slot_mapping, uint16_t* k_cache_w, uint16_t* v_cache_w) {
   using Sh = DecodeShape<D>;
   // W V slices of kLdsWave elements while streaming; the merge stage after.
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -544,16 +567,32 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int64_t kv_row = (int64_t)Hkv * D;
+  NewToken nt{-1, nullptr, nullptr};
+  if constexpr (kWrite) {
+    // A negative slot writes nothing, and the token is then read from the
+    // cache like every other, as a separate write launch would leave it.
+    const int64_t slot = slot_mapping[t0];
+    if (slot >= 0) {
+      nt = NewToken{L - 1, knew + ((int64_t)t0 * Hkv + g) * D, vnew + ((int64_t)t0 * Hkv + g) * D};
+      if (part == nparts - 1 && w == 0 && lane < 2 * (D / 8)) {
+        // [NB, 16, Hkv, D]: the slot's row starts at element slot * Hkv * D
+        const int c8 = lane % (D / 8);
+        const bool isv = lane >= D / 8;
+        const u32x4 val = *(const u32x4*)((isv ? nt.v : nt.k) + c8 * 8);
+        *(u32x4*)((isv ? v_cache_w : k_cache_w) + slot * kv_row + (int64_t)g * D + c8 * 8) = val;
+      }
+    }
+  }
 
   WaveAcc<D> acc;
   acc.init();
   if (nmine > 0) {
     bf16x8 qv[Sh::kKChunks];
     load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G);
-    stream_blocks<D, NBUF, kStreamV>(
+    stream_blocks<D, NBUF, kStreamV, kWrite>(
         acc, qv, my_blk, nmine, (b_begin + w) * kBlock, W * kBlock, tok_end,
         k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row, v_cache + (int64_t)g * D,
-        kv_row, lds + w * Sh::kLdsWave, scale_log2, lane);
+        kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt);
     acc.lsum = sum_across_groups(acc.lsum);
   }
 
@@ -660,12 +699,22 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
   dim3 grid(a.num_seqs, a.num_kv_heads, p.num_parts_max);
   const size_t lds = (size_t)p.waves * Sh::kLdsWave * sizeof(uint16_t);
   profile_begin(PA_KERNEL_DECODE, stream);
-  hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV>), grid, dim3(p.waves * kWave), lds,
-                     stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
-                     (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
-                     (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
-                     a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max);
+  if (p.fused_write) {
+    hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, true>), grid, dim3(p.waves * kWave), lds,
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                       (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
+                       (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
+                       a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
+                       (const uint16_t*)p.knew, (const uint16_t*)p.vnew, p.slot_mapping,
+                       (uint16_t*)p.k_cache_w, (uint16_t*)p.v_cache_w);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, false>), grid, dim3(p.waves * kWave),
+                       lds, stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
+                       (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
+                       (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
+                       a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
+                       nullptr, nullptr, nullptr, nullptr, nullptr);
+  }
   profile_end(PA_KERNEL_DECODE, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_parts_max <= 1) return e;
@@ -696,6 +745,9 @@ size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seq
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
   const int maxw = decode_max_waves(a.head_size, p.prefetch);
   if (p.waves < 1 || p.waves > maxw || a.num_kv_heads > 65535) return hipErrorInvalidValue;
+  if (p.fused_write && (p.stream || !p.knew || !p.vnew || !p.slot_mapping || !p.k_cache_w ||
+                        !p.v_cache_w))
+    return hipErrorInvalidValue;
   if (p.stream) {
     if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||
         decode_stream_lds_bytes(a.head_size, p.waves, a.num_seqs) > 64 * 1024)

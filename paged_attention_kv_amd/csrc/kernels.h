@@ -50,6 +50,14 @@ struct DecodePlan {
   float* ws_o;            // partial outputs: stream [wgs][2][Hq][D], partitioned [S][parts][Hq][D]
   float* ws_ml;           // partial (max in log2 units, sum): same rows, 2 floats each
   int32_t* counters;      // stream: [S][groups] arrival counters, zero between calls
+  // Fused write (partitioned schedule, decode rows only): the decode launch
+  // also writes each row's new token and reads it from knew / vnew.
+  bool fused_write;
+  const void* knew;
+  const void* vnew;
+  const int64_t* slot_mapping;
+  void* k_cache_w;
+  void* v_cache_w;
 };
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream);
 // Most waves a decode workgroup may hold for this head size and ring depth

@@ -247,14 +247,30 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
                        workspace, workspace_bytes, 0u, stream);
 }
 
-int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
-                  const int32_t* block_table, const int32_t* seq_lens,
-                  const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
-                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
-                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-                  int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
-                  size_t workspace_bytes, uint32_t flags, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+
+// The step's KV write when it travels with the forward (pa_write_and_forward).
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  const int64_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+};
+
+// pa_forward_ex, optionally preceded by the step's KV write (wr): fused into
+// the decode launch when every row is a decode row (max_query_len_hint == 1)
+// and the rows take the partitioned schedule, else a cache-write launch
+// first.
+int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, const int32_t* seq_lens,
+                 const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
+                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                 int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                 int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                 size_t workspace_bytes, uint32_t flags, void* stream) {
   const uint32_t known =
       PA_FORWARD_SHARED_BLOCKS | PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED;
   if (flags & ~known)
@@ -319,6 +335,17 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
 
+  pa::DecodePlan dp;
+  dp.stream = (flags & PA_FORWARD_DECODE_EVEN_SHARES)  ? w.stream_ok
+              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
+                                                        : w.stream_default;
+  const bool fused = wr && max_query_len_hint == 1 && !dp.stream;
+  if (wr && !fused) {
+    hipError_t e = pa::launch_cache_write(wr->k, wr->v, wr->slot_mapping, wr->k_cache,
+                                          wr->v_cache, num_tokens, num_kv_heads, head_size, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward cache write launch");
+  }
+
   if (a.max_query_len > 1) {
     pa::PrefillPlan pp;
     pp.tile_queries = w.tile_queries;
@@ -335,10 +362,6 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
     hipError_t e = pa::launch_prefill(a, pp, st);
     if (e != hipSuccess) return hip_fail(e, "pa_forward prefill launch");
   }
-  pa::DecodePlan dp;
-  dp.stream = (flags & PA_FORWARD_DECODE_EVEN_SHARES)  ? w.stream_ok
-              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
-                                                        : w.stream_default;
   dp.stream_wgs = w.stream_wgs;
   dp.stream_heads = w.stream_heads;
   dp.part_tokens = w.part_tokens;
@@ -349,10 +372,57 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
   dp.counters = (int32_t*)(ws + w.off_ctr);
+  dp.fused_write = fused;
+  dp.knew = fused ? wr->k : nullptr;
+  dp.vnew = fused ? wr->v : nullptr;
+  dp.slot_mapping = fused ? wr->slot_mapping : nullptr;
+  dp.k_cache_w = fused ? wr->k_cache : nullptr;
+  dp.v_cache_w = fused ? wr->v_cache : nullptr;
   hipError_t e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward decode launch");
   return PA_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* seq_lens,
+                  const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                  int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                  size_t workspace_bytes, uint32_t flags, void* stream) {
+  g_last_error.clear();
+  return forward_impl(nullptr, q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                      out, num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                      max_blocks_per_seq, num_blocks, max_query_len_hint, max_seq_len_hint,
+                      workspace, workspace_bytes, flags, stream);
+}
+
+int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mapping,
+                         void* k_cache, void* v_cache, const void* q, const int32_t* block_table,
+                         const int32_t* seq_lens, const int32_t* query_start_loc, float scale,
+                         void* out, int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks,
+                         int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                         size_t workspace_bytes, uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (num_tokens > 0) {
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+      return fail(PA_ERR_NULL, "pa_write_and_forward: null k/v/slot_mapping/cache");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_ALIGN, "pa_write_and_forward: k and v must be 16-byte aligned");
+  }
+  const WriteArgs wr{k, v, slot_mapping, k_cache, v_cache};
+  return forward_impl(&wr, q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                      out, num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                      max_blocks_per_seq, num_blocks, max_query_len_hint, max_seq_len_hint,
+                      workspace, workspace_bytes, flags, stream);
+}
+
 
 int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* query_start_loc, const int64_t* slot_mapping,

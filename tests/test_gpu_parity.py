@@ -256,6 +256,97 @@ def test_decode_schedules(name, hq, hkv, d, rows, schedule):
     assert_close(out.cpu()[r], want, name)
 
 
+# ---------------------------------------------------------------------------
+# Write and forward in one call
+# ---------------------------------------------------------------------------
+
+def fused_call(case, schedule=None, max_query_len=1, **kw):
+    out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
+                               case.q, case.block_table, case.seq_lens, case.query_start_loc,
+                               case.scale, max_query_len=max_query_len,
+                               max_seq_len=max(case.spec.seq_lens), decode_schedule=schedule,
+                               **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+FUSED_CASES = [
+    # name, Hq, Hkv, D, rows
+    ("d128_g4", 32, 8, 128, [(1, 1 + (37 * i) % 3000) for i in range(40)] + [(1, 1), (1, 16),
+                                                                           (1, 17), (1, 4096)]),
+    ("d64_g8", 64, 8, 64, [(1, 1 + (53 * i) % 2100) for i in range(33)]),
+    ("mqa16", 16, 1, 128, [(1, 2000), (1, 500), (1, 3)]),
+    ("kv16_g1", 16, 16, 64, [(1, 300), (1, 1000), (1, 77), (0, 12), (1, 9000)]),
+]
+
+
+@pytest.mark.parametrize("schedule", [None, "partitioned", "even"])
+@pytest.mark.parametrize("name,hq,hkv,d,rows", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_write_and_forward_decode_rows(name, hq, hkv, d, rows, schedule):
+    """Decode rows only (max_query_len 1): the cache ends bit-exact as
+    ref_cache_write leaves it (the new-token slots held poison before), the
+    output matches the oracle, and is bit-identical to cache_write followed
+    by forward on the same schedule. The partitioned schedule does it in one
+    launch (no cache-write launch recorded)."""
+    spec = wl.custom(name, hq, hkv, d, rows=rows, seed=80 + len(rows))
+    banner(f"write_and_forward {name} ({schedule}): S={spec.num_seqs} Hq={hq} Hkv={hkv} D={d}")
+    case = wl.make_case(spec, device=DEV)
+    kc_ref, vc_ref = case.k_cache.cpu(), case.v_cache.cpu()
+    oracle.ref_cache_write(case.k.cpu(), case.v.cpu(), case.slot_mapping.cpu(), kc_ref, vc_ref)
+    pa.profile_begin()
+    out = fused_call(case, schedule).clone()
+    per = pa.profile_end()
+    launches = {c: n for c, (n, _) in per.items()}
+    if schedule == "partitioned":
+        assert launches.get("cache_write", 0) == 0 and launches["decode"] == 1, per
+    else:
+        assert launches["decode"] >= 1, per
+    assert torch.equal(case.k_cache.cpu().view(torch.int16), kc_ref.view(torch.int16))
+    assert torch.equal(case.v_cache.cpu().view(torch.int16), vc_ref.view(torch.int16))
+    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
+    r, want = oracle_rows(case, seqs)
+    assert_close(out.cpu()[r], want, name)
+    # the same step as two calls (the cache already holds the new tokens,
+    # and rewriting them changes nothing)
+    two = write_and_forward(case, decode_schedule=schedule)
+    assert torch.equal(out.view(torch.int16), two.view(torch.int16)), "fused != two calls"
+
+
+def test_write_and_forward_skips_negative_slots():
+    """Tokens with slot < 0 are not written and their rows read the cache
+    (here poison at the new position), exactly as the two-call sequence."""
+    rows = [(1, 40), (1, 17), (1, 300), (1, 16), (1, 1)]
+    spec = wl.custom("neg_fused", 32, 8, 128, rows=rows, seed=91)
+    case = wl.make_case(spec, device=DEV)
+    slots = case.slot_mapping.clone()
+    slots[1] = -1
+    slots[3] = -7
+    case.slot_mapping = slots
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    out = fused_call(case, "partitioned").clone()
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    case.k_cache.copy_(k0)
+    case.v_cache.copy_(v0)
+    two = write_and_forward(case, decode_schedule="partitioned")
+    assert torch.equal(kc.view(torch.int16), case.k_cache.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), case.v_cache.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), two.view(torch.int16))
+    r, want = oracle_rows(case, [0, 2, 4])
+    assert_close(out.cpu()[r], want, "rows with slots")
+
+
+def test_write_and_forward_mixed_batch_falls_back_to_two_launches():
+    rows = [(1, 900), (37, 100), (1, 33), (200, 200), (1, 5000)]
+    spec = wl.custom("mixed_fused", 32, 8, 128, rows=rows, seed=92)
+    case = wl.make_case(spec, device=DEV)
+    pa.profile_begin()
+    out = fused_call(case, max_query_len=200)
+    per = pa.profile_end()
+    assert per["cache_write"][0] == 1 and per["prefill"][0] == 1 and per["decode"][0] == 1
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "mixed")
+
+
 def test_nan_poison_outside_context_does_not_leak():
     rows = [(1, 18), (7, 9), (1, 31), (40, 0), (1, 1)]
     spec = wl.custom("nanpoison", 32, 8, 128, rows=rows, seed=42)
