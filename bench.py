@@ -136,10 +136,10 @@ class StepInputs:
                           shared_blocks=spec.shared_prefix_blocks > 0)
 
 
-FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan")
+FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan", "prefix")
 
 
-def run_steps(pa, inp: StepInputs, steps: int, warmup: int):
+def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool = False):
     """Time `steps` steps (KV write + forward). Pass 1 is bracketed by
     synchronize and timed with HIP events on the launch stream, with nothing
     else inside (the step time). Pass 2 repeats the steps with the library's
@@ -151,6 +151,13 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int):
 
     def step(i):
         st = inp.sets[i % inp.rotations]
+        if shared_prefix:
+            # the write, then the shared prefix attended once for all rows
+            pa.cache_write(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache)
+            pa.forward_shared_prefix(st["q"], inp.k_cache, inp.v_cache, st["block_table"],
+                                     inp.seq_lens, inp.qsl, spec.scale, spec.shared_prefix_blocks,
+                                     out=st["out"], max_seq_len=inp.hints["max_seq_len"])
+            return
         pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
                              st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
                              out=st["out"], **inp.hints)
@@ -346,6 +353,14 @@ def main(argv=None):
                     spec.max_blocks_per_seq - spec.shared_prefix_blocks)) * \
                     2 * spec.block_size * spec.num_kv_heads * spec.head_size * 2
                 entry["forward_gbs_unique"] = round(uniq / (ms_fwd * 1e-3) / 1e9, 2)
+                # the same step through pa_forward_shared_prefix
+                ms2, km2, _, fwd2 = run_steps(pa, inp, args.steps, args.warmup, shared_prefix=True)
+                entry["shared_prefix_pass"] = {
+                    "ms_per_step": round(ms2, 5), "ms_forward_kernels": round(fwd2, 5),
+                    "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in km2.items()},
+                    "forward_gbs_logical": round(b / (fwd2 * 1e-3) / 1e9, 2),
+                    "forward_gbs_unique": round(uniq / (fwd2 * 1e-3) / 1e9, 2),
+                    "tokens_per_s": round(spec.num_tokens / (ms2 * 1e-3), 1)}
             if i == 4:
                 entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
             others.append((name, entry))

@@ -221,6 +221,45 @@ int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mappi
                          size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * Decode rows whose tables all begin with the same prefix_blocks blocks
+ * (a shared prompt prefix; section "Prefix Caching": a cached block is
+ * referenced by every request that shares it). The prefix's keys are
+ * attended once for all rows together: their query tokens are stacked as
+ * the rows of matrix-core tiles (G heads each), chunk by chunk of the
+ * prefix, leaving partial results per row; each row's own blocks after the
+ * prefix run on the partitioned decode schedule; a merge pass combines both
+ * (the log-sum-exp identity). Results agree with pa_forward_ex to rounding
+ * order.
+ *
+ *   q ... out, sizes, num_blocks   as for pa_forward_ex, with num_tokens =
+ *                    num_seqs: every row is a decode row (query_start_loc
+ *                    = 0, 1, ..., num_seqs)
+ *   prefix_blocks    leading table entries shared by every row (>= 1);
+ *                    row 0's entries are the ones read
+ *   max_seq_len_hint as for pa_forward_ex; must exceed 16 * prefix_blocks
+ *   workspace        >= pa_shared_prefix_workspace_bytes(...) bytes, 16-byte
+ *                    aligned; scratch written before it is read
+ *   flags            0 or PA_FORWARD_SHARED_BLOCKS
+ *
+ * Caller contract (not checked): every row's first prefix_blocks table
+ * entries equal row 0's, and seq_lens[s] > 16 * prefix_blocks (the row's
+ * new token lies past the prefix, in a block of its own). Errors as for
+ * pa_forward_ex; on an error nothing is launched.
+ */
+size_t pa_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t max_blocks_per_seq, int32_t prefix_blocks,
+                                        int32_t max_seq_len_hint);
+int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, float scale, void* out,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, int32_t prefix_blocks, int32_t max_seq_len_hint,
+                             void* workspace, size_t workspace_bytes, uint32_t flags,
+                             void* stream);
+
+/*
  * Synchronous check of the device-resident metadata that the hot path
  * trusts (for tests and debugging; copies to the host and waits on
  * `stream`). Checks: query_start_loc starts at 0, never decreases and ends at
@@ -252,6 +291,7 @@ int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
 #define PA_KERNEL_PREFILL 3       /* prefill tiles seeing many keys            */
 #define PA_KERNEL_PREFILL_SHORT 4 /* prefill tiles seeing few keys             */
 #define PA_KERNEL_PLAN 5          /* prefill tile planner                      */
+#define PA_KERNEL_PREFIX 6        /* shared-prefix pass (pa_forward_shared_prefix) */
 #define PA_KERNEL_CLASSES 8
 
 typedef struct pa_profile {

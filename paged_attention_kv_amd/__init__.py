@@ -16,7 +16,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["cache_write", "forward", "write_and_forward", "forward_workspace_bytes",
+__all__ = ["cache_write", "forward", "write_and_forward", "forward_shared_prefix",
+           "forward_workspace_bytes",
            "validate_inputs",
            "kv_block_bytes", "last_error", "version", "library_path", "load_library",
            "profile_begin", "profile_end", "PaError", "BLOCK_SIZE", "KERNEL_CLASSES"]
@@ -45,6 +46,10 @@ SIGNATURES = {
     "pa_kv_block_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "pa_cache_write": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P]),
     "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_forward_shared_prefix": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                                _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
+                                                _I32, _P, _SZ, ctypes.c_uint32, _P]),
     "pa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32,
                                   _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
     "pa_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
@@ -64,7 +69,7 @@ SIGNATURES = {
 
 # Kernel classes of the timing facility (PA_KERNEL_* in include/pa.h).
 KERNEL_CLASSES = {0: "cache_write", 1: "decode", 2: "combine", 3: "prefill",
-                  4: "prefill_short", 5: "plan"}
+                  4: "prefill_short", 5: "plan", 6: "prefix"}
 _NCLASS = 8
 
 
@@ -238,6 +243,55 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                               decode_schedule)
     _check(load_library().pa_forward_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                          *tail))
+    return out
+
+
+def forward_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          query_start_loc: torch.Tensor, scale: float, prefix_blocks: int,
+                          out: Optional[torch.Tensor] = None,
+                          max_seq_len: Optional[int] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          shared_blocks: bool = False) -> torch.Tensor:
+    """Decode rows (one query token each) whose tables all start with the
+    same ``prefix_blocks`` blocks (pa_forward_shared_prefix): the prefix is
+    attended once for all rows, each row's own blocks after it separately,
+    and the two merged. Returns ``out`` ([S, Hq, D] bf16)."""
+    lib = load_library()
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(n, t, torch.bfloat16, 4)
+    _dev_tensor("block_table", block_table, torch.int32, 2)
+    _dev_tensor("seq_lens", seq_lens, torch.int32, 1)
+    _dev_tensor("query_start_loc", query_start_loc, torch.int32, 1)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, Dc = k_cache.shape
+    S, MB = block_table.shape
+    if v_cache.shape != k_cache.shape or Dc != D:
+        raise ValueError("caches must be [NB, 16, Hkv, D] with q's head size")
+    if T != S or seq_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("one query token per row: q [S, Hq, D], seq_lens [S], "
+                         "query_start_loc [S+1]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _dev_tensor("out", out, torch.bfloat16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    need = lib.pa_shared_prefix_workspace_bytes(S, Hq, Hkv, D, MB, prefix_blocks,
+                                                max_seq_len or 0)
+    if need == 0:
+        raise ValueError("unsupported sizes for pa_forward_shared_prefix")
+    if workspace is None:
+        workspace = _workspace(q.device, need)
+    elif workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
+    _check(lib.pa_forward_shared_prefix(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), query_start_loc.data_ptr(), float(scale), out.data_ptr(), S, Hq,
+        Hkv, D, bs, MB, NB, prefix_blocks, max_seq_len or 0, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(),
+        FORWARD_SHARED_BLOCKS if shared_blocks else 0, _stream(q)))
     return out
 
 

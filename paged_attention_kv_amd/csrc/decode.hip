@@ -531,7 +531,8 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     float scale_log2, int32_t Hq, int32_t Hkv, int32_t G, int32_t MB, int32_t part_tokens,
-    int32_t num_parts_max, const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
+    int32_t num_parts_max, int32_t tok_base, int32_t part_base,
+    const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
     const int64_t* __restrict__ slot_mapping, uint16_t* k_cache_w, uint16_t* v_cache_w) {
   using Sh = DecodeShape<D>;
   // W V slices of kLdsWave elements while streaming; the merge stage after.
@@ -549,8 +550,10 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   // Block ids of this wave (lane k: partition block w + k*W), read before
   // the row's length is known so the loads overlap; the index is kept inside
   // the row, and lanes past the wave's blocks are never used.
+  // Keys from tok_base on (a multiple of 16: after a shared-prefix pass the
+  // prefix's partials are already in the workspace).
   const int bpp = part_tokens / kBlock;
-  const int b_begin = part * bpp;
+  const int b_begin = tok_base / kBlock + part * bpp;
   const int jb = w + lane * W;
   const int my_blk = (jb < bpp && b_begin + jb < MB)
                          ? block_table[(int64_t)s * MB + b_begin + jb] : 0;
@@ -558,10 +561,10 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   const int t0 = qsl[s];
   if (qsl[s + 1] - t0 != 1) return;  // not a decode row
   const int L = seq_lens[s];
-  const int tok_begin = part * part_tokens;
+  const int tok_begin = tok_base + part * part_tokens;
   if (tok_begin >= L) return;
   const int tok_end = min(L, tok_begin + part_tokens);
-  const int nparts = (L + part_tokens - 1) / part_tokens;
+  const int nparts = (L - tok_base + part_tokens - 1) / part_tokens;
   const int nblk = (tok_end + kBlock - 1) / kBlock - b_begin;
   const int nmine = nblk > w ? (nblk - 1 - w) / W + 1 : 0;  // blocks of this wave
   const int hl = lane & 15;
@@ -599,11 +602,11 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   merge_waves<D>(acc, (float*)lds, W, 1, G, w, lane,
                  [&](int, int col, int d, float M, float den, float n0, float n1) {
     const int qh = g * G + col;
-    if (nparts == 1) {
+    if (nparts == 1 && part_base == 0) {
       const float inv = 1.0f / den;
       *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
     } else {  // read by the combine kernel after this one ends
-      const int64_t base = ((int64_t)s * num_parts_max + part) * Hq + qh;
+      const int64_t base = ((int64_t)s * num_parts_max + part_base + part) * Hq + qh;
       *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
       if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
     }
@@ -616,7 +619,8 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
-    int32_t Hq, int32_t part_tokens, int32_t num_parts_max) {
+    int32_t Hq, int32_t part_tokens, int32_t num_parts_max, int32_t tok_base,
+    int32_t part_base) {
   constexpr int kPer = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int s = blockIdx.x;
@@ -625,7 +629,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int t0 = qsl[s];
   if (qsl[s + 1] - t0 != 1) return;
   const int L = seq_lens[s];
-  const int np = (L + part_tokens - 1) / part_tokens;
+  // partials 0 .. part_base-1 come from the shared-prefix pass
+  // (clamped to the workspace rows: a length past the planned maximum is a
+  // caller error, and reads stay inside the row's partials)
+  const int np =
+      min(num_parts_max, part_base + max(0, (L - tok_base + part_tokens - 1) / part_tokens));
   if (np <= 1) return;
   const int64_t row0 = (int64_t)s * num_parts_max * Hq + qh;  // partition p at row0 + p*Hq
 
@@ -696,7 +704,7 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
     profile_end(PA_KERNEL_DECODE, stream);
     return hipGetLastError();
   }
-  dim3 grid(a.num_seqs, a.num_kv_heads, p.num_parts_max);
+  dim3 grid(a.num_seqs, a.num_kv_heads, p.num_parts_max - p.part_base);
   const size_t lds = (size_t)p.waves * Sh::kLdsWave * sizeof(uint16_t);
   profile_begin(PA_KERNEL_DECODE, stream);
   if (p.fused_write) {
@@ -705,15 +713,15 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       (const uint16_t*)p.knew, (const uint16_t*)p.vnew, p.slot_mapping,
-                       (uint16_t*)p.k_cache_w, (uint16_t*)p.v_cache_w);
+                       p.tok_base, p.part_base, (const uint16_t*)p.knew, (const uint16_t*)p.vnew,
+                       p.slot_mapping, (uint16_t*)p.k_cache_w, (uint16_t*)p.v_cache_w);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, false>), grid, dim3(p.waves * kWave),
                        lds, stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       nullptr, nullptr, nullptr, nullptr, nullptr);
+                       p.tok_base, p.part_base, nullptr, nullptr, nullptr, nullptr, nullptr);
   }
   profile_end(PA_KERNEL_DECODE, stream);
   hipError_t e = hipGetLastError();
@@ -722,7 +730,7 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
   profile_begin(PA_KERNEL_COMBINE, stream);
   hipLaunchKernelGGL(decode_combine_kernel<D>, cgrid, dim3(256), 0, stream, a.seq_lens,
                      a.query_start_loc, p.ws_o, p.ws_ml, (uint16_t*)a.out, a.num_q_heads,
-                     p.part_tokens, p.num_parts_max);
+                     p.part_tokens, p.num_parts_max, p.tok_base, p.part_base);
   profile_end(PA_KERNEL_COMBINE, stream);
   return hipGetLastError();
 }
@@ -747,6 +755,9 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
   if (p.waves < 1 || p.waves > maxw || a.num_kv_heads > 65535) return hipErrorInvalidValue;
   if (p.fused_write && (p.stream || !p.knew || !p.vnew || !p.slot_mapping || !p.k_cache_w ||
                         !p.v_cache_w))
+    return hipErrorInvalidValue;
+  if (p.tok_base < 0 || p.tok_base % kBlock || p.part_base < 0 ||
+      p.num_parts_max - p.part_base < 1 || ((p.tok_base || p.part_base) && p.stream))
     return hipErrorInvalidValue;
   if (p.stream) {
     if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||

@@ -50,6 +50,11 @@ struct DecodePlan {
   float* ws_o;            // partial outputs: stream [wgs][2][Hq][D], partitioned [S][parts][Hq][D]
   float* ws_ml;           // partial (max in log2 units, sum): same rows, 2 floats each
   int32_t* counters;      // stream: [S][groups] arrival counters, zero between calls
+  // Partitioned schedule after a shared-prefix pass: keys start at
+  // tok_base, partition p is stored as partial part_base + p, and every row
+  // leaves partials for the combine (even with one partition).
+  int32_t tok_base;
+  int32_t part_base;
   // Fused write (partitioned schedule, decode rows only): the decode launch
   // also writes each row's new token and reads it from knew / vnew.
   bool fused_write;
@@ -83,6 +88,19 @@ int32_t prefill_tile_queries(int32_t group);
 int32_t prefill_split_tile_queries(int32_t group);
 // Upper bound on list-B tiles per row.
 int32_t prefill_split_tiles_per_row(int32_t group);
+
+// Shared-prefix pass: the first prefix_keys keys of every decode row come
+// from the same blocks (row 0's table); chunks of chunk_keys keys are
+// attended for all rows at once and leave partials 0 .. chunks-1 of each row.
+struct PrefixPlan {
+  int32_t chunks;
+  int32_t chunk_keys;     // multiple of 64
+  int32_t prefix_keys;    // 16 * prefix blocks
+  int32_t num_parts_max;  // partials per row in the workspace (prefix + suffix)
+  float* ws_o;
+  float* ws_ml;
+};
+hipError_t launch_prefix(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream);
 
 // Workspace layout shared by pa_forward and pa_forward_workspace_bytes.
 struct WorkspaceLayout {

@@ -372,6 +372,8 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
   dp.counters = (int32_t*)(ws + w.off_ctr);
+  dp.tok_base = 0;
+  dp.part_base = 0;
   dp.fused_write = fused;
   dp.knew = fused ? wr->k : nullptr;
   dp.vnew = fused ? wr->v : nullptr;
@@ -423,6 +425,169 @@ int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mappi
                       workspace, workspace_bytes, flags, stream);
 }
 
+
+}  // extern "C"
+
+namespace {
+
+// Shared-prefix decode: the prefix pass covers the first prefix_blocks
+// blocks of every row in chunks; each row's remaining keys run on the
+// partitioned decode schedule; the combine merges both.
+struct PrefixLayout {
+  int32_t chunks, chunk_keys, prefix_keys, waves, prefetch, part_tokens, suffix_parts,
+      num_parts_max;
+  size_t off_o, off_ml, total;
+};
+// Prefix workgroups aimed for: one per CU; chunks of at least 512 keys.
+constexpr int32_t kPrefixMinChunkKeys = 512;
+
+bool plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                 int32_t max_blocks_per_seq, int32_t prefix_blocks, int32_t max_seq_len_hint,
+                 PrefixLayout* out) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads || prefix_blocks <= 0 ||
+      prefix_blocks >= max_blocks_per_seq)
+    return false;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!supported_group(group)) return false;
+  const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
+  PrefixLayout p;
+  p.prefix_keys = prefix_blocks * PA_BLOCK_SIZE;
+  if (max_len <= p.prefix_keys) return false;
+  const int32_t rows = pa::prefill_tile_queries(group);
+  const int64_t row_tiles = (num_seqs + rows - 1) / rows;
+  const int64_t want = std::max<int64_t>(1, (kComputeUnits + row_tiles * num_kv_heads - 1) /
+                                                (row_tiles * num_kv_heads));
+  const int64_t most = std::max<int64_t>(1, (p.prefix_keys + kPrefixMinChunkKeys - 1) /
+                                                kPrefixMinChunkKeys);
+  const int64_t chunks = std::min(want, most);
+  p.chunk_keys = (int32_t)(((p.prefix_keys + chunks - 1) / chunks + 63) / 64 * 64);
+  p.chunks = (p.prefix_keys + p.chunk_keys - 1) / p.chunk_keys;
+  p.prefetch = decode_prefetch(head_size);
+  p.waves = decode_waves(head_size, p.prefetch);
+  const int32_t suffix_len = max_len - p.prefix_keys;
+  p.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, p.waves, suffix_len);
+  p.suffix_parts = (suffix_len + p.part_tokens - 1) / p.part_tokens;
+  p.num_parts_max = p.chunks + p.suffix_parts;
+  if (p.suffix_parts > kMaxGridZ) return false;
+  const size_t prow = (size_t)num_seqs * p.num_parts_max * num_q_heads;
+  p.off_o = round_up((size_t)kCounterSlots * sizeof(int32_t), kAlign);
+  p.off_ml = round_up(p.off_o + prow * head_size * sizeof(float), kAlign);
+  p.total = round_up(p.off_ml + prow * 2 * sizeof(float), kAlign);
+  *out = p;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t max_blocks_per_seq, int32_t prefix_blocks,
+                                        int32_t max_seq_len_hint) {
+  PrefixLayout p;
+  if (!plan_prefix(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq,
+                   prefix_blocks, max_seq_len_hint, &p))
+    return 0;
+  return p.total;
+}
+
+int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const int32_t* query_start_loc, float scale, void* out,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                             int64_t num_blocks, int32_t prefix_blocks, int32_t max_seq_len_hint,
+                             void* workspace, size_t workspace_bytes, uint32_t flags,
+                             void* stream) {
+  g_last_error.clear();
+  if (flags & ~PA_FORWARD_SHARED_BLOCKS)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: unsupported flags 0x%x", flags);
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: a size is out of range");
+  if (num_q_heads % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: num_q_heads %d is not a multiple of "
+                "num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: block_size %d (only %d is "
+                "built)", block_size, PA_BLOCK_SIZE);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: head_size %d (built: 64, 128)",
+                head_size);
+  if (!supported_group(num_q_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: %d query heads per KV head",
+                num_q_heads / num_kv_heads);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: scale is not finite");
+  const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
+  if (prefix_blocks <= 0 || (int64_t)prefix_blocks * PA_BLOCK_SIZE >= max_len)
+    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: prefix_blocks %d must be >= 1 and "
+                "leave every row at least one key past it (max_seq_len %d)", prefix_blocks,
+                max_len);
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
+    return fail(PA_ERR_NULL, "pa_forward_shared_prefix: null pointer argument");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
+    return fail(PA_ERR_ALIGN, "pa_forward_shared_prefix: q, caches and out must be 16-byte "
+                "aligned");
+  PrefixLayout pl;
+  if (!plan_prefix(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq,
+                   prefix_blocks, max_seq_len_hint, &pl))
+    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: cannot plan the workspace");
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(PA_ERR_WORKSPACE, "pa_forward_shared_prefix: workspace of %zu bytes, %zu "
+                "needed", workspace ? workspace_bytes : (size_t)0, pl.total);
+  if (!aligned(workspace, 16))
+    return fail(PA_ERR_ALIGN, "pa_forward_shared_prefix: workspace must be 16-byte aligned");
+
+  pa::ForwardArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.out = out;
+  a.scale = scale;
+  a.num_tokens = num_seqs;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = max_len;
+  a.max_query_len = 1;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  pa::PrefixPlan pp;
+  pp.chunks = pl.chunks;
+  pp.chunk_keys = pl.chunk_keys;
+  pp.prefix_keys = pl.prefix_keys;
+  pp.num_parts_max = pl.num_parts_max;
+  pp.ws_o = (float*)(ws + pl.off_o);
+  pp.ws_ml = (float*)(ws + pl.off_ml);
+  hipError_t e = pa::launch_prefix(a, pp, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix prefix launch");
+
+  pa::DecodePlan dp = {};
+  dp.stream = false;
+  dp.part_tokens = pl.part_tokens;
+  dp.num_parts_max = pl.num_parts_max;
+  dp.waves = pl.waves;
+  dp.prefetch = pl.prefetch;
+  dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
+  dp.ws_o = pp.ws_o;
+  dp.ws_ml = pp.ws_ml;
+  dp.tok_base = pl.prefix_keys;
+  dp.part_base = pl.chunks;
+  e = pa::launch_decode(a, dp, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix decode launch");
+  return PA_OK;
+}
 
 int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* query_start_loc, const int64_t* slot_mapping,

@@ -151,14 +151,37 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
-template <int D, int G, bool SPLIT>
-__global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefill_tile_kernel(
+// Kernel modes: the two prefill tile lists, and the shared-prefix pass.
+enum TileMode { kListA = 0, kListB = 1, kPrefix = 2 };
+
+// Shared-prefix pass (PREFIX): the rows of a tile are the single query
+// tokens of consecutive decode rows (G heads each), the keys one chunk of
+// the prefix that every row's table starts with (read through row 0's
+// table); no mask applies (every row sees the whole prefix), and the tile
+// leaves unnormalised fp32 partials (numerator, reference max, weight sum)
+// as partition `chunk` of each row for the decode combine.
+struct PrefixArgs {
+  float* ws_o;            // [S][num_parts_max][Hq][D]
+  float* ws_ml;           // [S][num_parts_max][Hq][2]
+  int32_t num_parts_max;
+  int32_t chunk_keys;     // keys per chunk (multiple of 64)
+  int32_t prefix_keys;    // 16 * prefix blocks
+  int32_t num_seqs;
+  int32_t row_tiles;      // ceil(num_seqs / tile rows)
+  int32_t chunks;
+  int32_t num_tokens;     // q rows (a row's token index is clamped below it)
+};
+
+template <int D, int G, int MODE>
+__global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) void prefill_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ tile_count, float scale_log2, int32_t Hq, int32_t Hkv,
-    int32_t MB, int32_t tile_bound) {
+    int32_t MB, int32_t tile_bound, PrefixArgs pfx) {
+  constexpr bool SPLIT = MODE == kListB;
+  constexpr bool PREFIX = MODE == kPrefix;
   constexpr int NW = SPLIT ? kWavesB : kWavesA;   // waves
   constexpr int NST = SPLIT ? kStagesB : kStagesA;  // LDS stages
   constexpr int BQ = 32 * NW / G;             // query tokens per tile
@@ -180,18 +203,38 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
   __shared__ __attribute__((aligned(1024))) uint8_t ks[NST][BN * RB];
   __shared__ __attribute__((aligned(1024))) uint8_t vs[NST][BN * RB];
 
-  // One (sequence, query tile, KV head) task.
+  // One task: (sequence, first query row, KV head) from a tile list, or
+  // (first row, prefix chunk, KV head) in the shared-prefix pass.
   auto run_tile = [&](const int s, const int q0, const int g) {
-  const int tq0 = qsl[s];
-  const int ql = qsl[s + 1] - tq0;
-  const int L = seq_lens[s];
-  const int c = L - ql;
-  const int nq = min(BQ, ql - q0);
-  const int kv_end = c + q0 + nq;  // keys [0, kv_end) are visible to some row
-  const int ntiles = (kv_end + BN - 1) / BN;
-  // Keys up to first_lim are visible to every row of the tile: key tiles
-  // that end at or below it need no mask.
-  const int first_lim = c + q0;
+  int tq0, nq, c, kv_end, ktb, first_lim;
+  const int32_t* table;
+  if constexpr (PREFIX) {
+    // rows s .. s+nq-1 (one token each); keys of chunk q0
+    tq0 = 0;
+    nq = min(BQ, pfx.num_seqs - s);
+    c = 0;
+    kv_end = min((q0 + 1) * pfx.chunk_keys, pfx.prefix_keys);
+    ktb = q0 * (pfx.chunk_keys / BN);
+    // every row sees the whole chunk; only keys past its end (in its last
+    // tile) are masked
+    first_lim = kv_end - 1;
+    table = block_table;
+  } else {
+    tq0 = qsl[s];
+    const int ql = qsl[s + 1] - tq0;
+    const int L = seq_lens[s];
+    c = L - ql;
+    nq = min(BQ, ql - q0);
+    kv_end = c + q0 + nq;  // keys [0, kv_end) are visible to some row
+    ktb = 0;
+    // Keys up to first_lim are visible to every row of the tile: key tiles
+    // that end at or below it need no mask.
+    first_lim = c + q0;
+    table = block_table + (int64_t)s * MB;
+  }
+  // key tiles ktb .. ktb+ntiles-1; below, kt counts from 0 and key tile
+  // ktb + kt holds keys (ktb + kt) * 64 ..
+  const int ntiles = (kv_end + BN - 1) / BN - ktb;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -208,10 +251,16 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
     const int row = w * 32 + mt * 16 + hl;
     const int tl = row / G;
     const int hh = row % G;
-    lim[mt] = c + q0 + min(tl, nq - 1);
     const bool ok = tl < nq;
-    const u32x4* qp =
-        (const u32x4*)(q + ((int64_t)(tq0 + q0 + (ok ? tl : 0)) * Hq + g * G + hh) * D) + grp;
+    int tok;
+    if constexpr (PREFIX) {
+      lim[mt] = kv_end - 1;
+      tok = min(qsl[s + (ok ? tl : 0)], pfx.num_tokens - 1);
+    } else {
+      lim[mt] = c + q0 + min(tl, nq - 1);
+      tok = tq0 + q0 + (ok ? tl : 0);
+    }
+    const u32x4* qp = (const u32x4*)(q + ((int64_t)tok * Hq + g * G + hh) * D) + grp;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
       const u32x4 z = {0u, 0u, 0u, 0u};
@@ -231,7 +280,6 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
   f32x4 lsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
-  const int32_t* table = block_table + (int64_t)s * MB;
   const int last_blk = (kv_end - 1) / kBlock;  // last block any row reads
   constexpr int kTileBlocks = BN / kBlock;     // 16-token blocks per key tile
   // Load op j of wave w fills LDS bytes (j*NW + w)*1024 .. +1024 of a stage:
@@ -241,7 +289,7 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
   auto kb = [&](int j) { return ((j * NW + w) * 1024 / RB) / kBlock; };
   auto tile_ids = [&](int kt, int (&ids)[NDMA]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) ids[j] = table[min(kt * kTileBlocks + kb(j), last_blk)];
+    for (int j = 0; j < NDMA; ++j) ids[j] = table[min((ktb + kt) * kTileBlocks + kb(j), last_blk)];
   };
   // Tile kt straight from HBM/L2 into LDS stage `stage`: lane l of op j
   // covers row r, physical chunk pc, and fetches logical chunk pc ^ swz(r)
@@ -268,7 +316,7 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const int p = (j * NW + w) * 1024 + lane * 16;
-      if (kt * BN + p / RB >= kv_end) *(u32x4*)(&vs[stage][p]) = u32x4{0u, 0u, 0u, 0u};
+      if ((ktb + kt) * BN + p / RB >= kv_end) *(u32x4*)(&vs[stage][p]) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -316,7 +364,7 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
         for (int n = 0; n < NS; ++n)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int key = kt * BN + n * 16 + 4 * grp + r;
+            const int key = (ktb + kt) * BN + n * 16 + 4 * grp + r;
             st[mt][n][r] = key <= lim[mt] ? st[mt][n][r] : -INFINITY;
           }
     }
@@ -430,12 +478,12 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
     const int later = min(NST - 2, ntiles - 1 - kt);  // tiles issued after kt
     if (NST == 3 && later == 1) wait_loads_then_barrier<kOps>();
     else wait_loads_then_barrier<0>();
-    if ((kt + 1) * BN > kv_end) {
+    if ((ktb + kt + 1) * BN > kv_end) {
       zero_tail(kt, stage);
       lds_writes_then_barrier();
     }
     if (kt + NST - 1 < ntiles) dma_tile((kt + NST - 1) % NST, ids);
-    const bool masked = (kt + 1) * BN - 1 > first_lim;
+    const bool masked = (ktb + kt + 1) * BN - 1 > first_lim;
     // Tiles whose rows see at most kSplitKeys keys (SPLIT) keep P to about
     // 2^-17 (hi + lo): few weights carry each output there, and bf16
     // rounding of P would show in it.
@@ -447,6 +495,23 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
     tile_ids(kt + NST, ids);
   }
 
+  if constexpr (PREFIX) {
+    // partition q0 (the chunk) of rows s + tl: unnormalised numerator,
+    // reference max (log2 units) and weight sum
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int row = w * 32 + mt * 16 + hl;
+      const int tl = row / G;
+      const int hh = row % G;
+      if (tl >= nq) continue;
+      const int64_t base = ((int64_t)(s + tl) * pfx.num_parts_max + q0) * Hq + g * G + hh;
+      float* op = pfx.ws_o + base * D + 4 * grp;
+#pragma unroll
+      for (int mi = 0; mi < DT; ++mi) *(f32x4*)(op + 16 * mi) = o[mt][mi];
+      if (grp == 0) *(f32x2*)(pfx.ws_ml + base * 2) = f32x2{m[mt], lsum[mt][0]};
+    }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const float ltot = lsum[mt][0];
@@ -466,7 +531,17 @@ __global__ __launch_bounds__((SPLIT ? kWavesB : kWavesA) * kWave, 1) void prefil
   };  // run_tile
 
   const int nwg = gridDim.x;
-  if (!SPLIT) {
+  if (PREFIX) {
+    // XCD-aware order: the row tiles of one (KV head, chunk) are
+    // consecutive logical tasks, so they share the chunk's K/V in one L2.
+    const int logical = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+    const int rt = logical % pfx.row_tiles;
+    const int rest = logical / pfx.row_tiles;
+    const int chunk = rest % pfx.chunks;
+    const int g = rest / pfx.chunks;
+    if (g >= Hkv) return;
+    run_tile(rt * BQ, chunk, g);
+  } else if (!SPLIT) {
     // XCD-aware order: consecutive logical tiles (same KV head, same
     // sequence) land on the same XCD and share its L2.
     const int logical = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
@@ -495,12 +570,12 @@ hipError_t launch_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t 
     const int64_t grid = ((int64_t)p.bound_a * a.num_kv_heads + 7) / 8 * 8;
     if (grid > INT32_MAX) return hipErrorInvalidValue;
     profile_begin(PA_KERNEL_PREFILL, stream);
-    hipLaunchKernelGGL((prefill_tile_kernel<D, G, false>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_tile_kernel<D, G, kListA>), dim3((unsigned)grid),
                        dim3(kWavesA * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_table,
                        a.seq_lens, a.query_start_loc, (uint16_t*)a.out, p.tiles_a, p.counts,
                        scale_log2, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq,
-                       p.bound_a);
+                       p.bound_a, PrefixArgs{});
     profile_end(PA_KERNEL_PREFILL, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -509,12 +584,12 @@ hipError_t launch_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t 
     const int64_t grid =
         std::min<int64_t>((int64_t)p.bound_b * a.num_kv_heads, kSplitGridMax);
     profile_begin(PA_KERNEL_PREFILL_SHORT, stream);
-    hipLaunchKernelGGL((prefill_tile_kernel<D, G, true>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((prefill_tile_kernel<D, G, kListB>), dim3((unsigned)grid),
                        dim3(kWavesB * kWave), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_table,
                        a.seq_lens, a.query_start_loc, (uint16_t*)a.out, p.tiles_b,
                        p.counts + 1, scale_log2, a.num_q_heads, a.num_kv_heads,
-                       a.max_blocks_per_seq, p.bound_b);
+                       a.max_blocks_per_seq, p.bound_b, PrefixArgs{});
     profile_end(PA_KERNEL_PREFILL_SHORT, stream);
     return hipGetLastError();
   }
@@ -533,7 +608,50 @@ hipError_t launch_tiles_d(const ForwardArgs& a, const PrefillPlan& p, hipStream_
   }
 }
 
+template <int D, int G>
+hipError_t launch_prefix_g(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream) {
+  constexpr int BQ = 32 * kWavesA / G;
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  PrefixArgs x{p.ws_o, p.ws_ml, p.num_parts_max, p.chunk_keys, p.prefix_keys, a.num_seqs,
+               (a.num_seqs + BQ - 1) / BQ, p.chunks, a.num_tokens};
+  const int64_t tasks = (int64_t)x.row_tiles * p.chunks * a.num_kv_heads;
+  const int64_t grid = (tasks + 7) / 8 * 8;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  profile_begin(PA_KERNEL_PREFIX, stream);
+  hipLaunchKernelGGL((prefill_tile_kernel<D, G, kPrefix>), dim3((unsigned)grid),
+                     dim3(kWavesA * kWave), 0, stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_table,
+                     a.seq_lens, a.query_start_loc, (uint16_t*)a.out, nullptr, nullptr,
+                     scale_log2, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, 0, x);
+  profile_end(PA_KERNEL_PREFIX, stream);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefix_d(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream) {
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_prefix_g<D, 1>(a, p, stream);
+    case 2: return launch_prefix_g<D, 2>(a, p, stream);
+    case 4: return launch_prefix_g<D, 4>(a, p, stream);
+    case 8: return launch_prefix_g<D, 8>(a, p, stream);
+    case 16: return launch_prefix_g<D, 16>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefix(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream) {
+  if (p.chunks < 1 || p.chunk_keys < kKeysPerTile || p.chunk_keys % kKeysPerTile ||
+      p.prefix_keys < 1 || (int64_t)p.chunks * p.chunk_keys < p.prefix_keys ||
+      p.num_parts_max <= p.chunks || !p.ws_o || !p.ws_ml)
+    return hipErrorInvalidValue;
+  switch (a.head_size) {
+    case 64: return launch_prefix_d<64>(a, p, stream);
+    case 128: return launch_prefix_d<128>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 int32_t prefill_tile_queries(int32_t group) { return 32 * kWavesA / group; }
 int32_t prefill_split_tile_queries(int32_t group) { return 32 * kWavesB / group; }

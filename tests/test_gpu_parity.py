@@ -173,6 +173,85 @@ def test_prefix_shared_sampled_rows(shared_flag):
 
 
 # ---------------------------------------------------------------------------
+# Shared-prefix decode (prefix attended once for all rows)
+# ---------------------------------------------------------------------------
+
+def shared_prefix_call(case, prefix_blocks, **kw):
+    pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
+    out = pa.forward_shared_prefix(case.q, case.k_cache, case.v_cache, case.block_table,
+                                   case.seq_lens, case.query_start_loc, case.scale, prefix_blocks,
+                                   max_seq_len=max(case.spec.seq_lens), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_shared_prefix_workload_sampled_rows():
+    """The prefix-shared decode workload (256 rows, 256 shared blocks + 8 own
+    blocks each): sampled rows against the oracle, and every row close to
+    the per-row decode path."""
+    spec = wl.config(5)
+    banner("shared-prefix pass on workload 5 (256 rows, 256-block shared prefix)")
+    case = wl.make_case(spec, device=DEV)
+    pa.profile_begin()
+    out = shared_prefix_call(case, spec.shared_prefix_blocks).clone()
+    per = pa.profile_end()
+    assert per["prefix"][0] == 1 and per["decode"][0] == 1 and per["combine"][0] == 1, per
+    pick = sorted(random.Random(15).sample(range(256), 14) + [0, 255])
+    rows, want = oracle_rows(case, pick)
+    assert_close(out.cpu()[rows], want, "shared prefix")
+    ref = write_and_forward(case, shared_blocks=True)
+    d = (out.float() - ref.float()).abs()
+    print(f"  vs per-row path: max {d.max().item():.3e} mean {d.mean().item():.3e}", flush=True)
+    assert d.max().item() <= 2 * MAX_ABS and d.mean().item() <= MEAN_ABS
+
+
+SHARED_PREFIX_CASES = [
+    # name, Hq, Hkv, D, prefix blocks, per-row own tokens after the prefix
+    ("d128_g4", 32, 8, 128, 40, [1, 2, 15, 16, 17, 100, 333, 1]),
+    ("d64_g8", 64, 8, 64, 19, [1 + (37 * i) % 200 for i in range(70)]),
+    ("one_block", 16, 4, 128, 1, [5, 1, 64, 300]),
+    ("g1_odd", 8, 8, 64, 33, [3, 250, 16]),
+    ("g16", 16, 1, 128, 70, [1, 7, 900]),
+    ("rows300", 32, 8, 128, 12, [1 + (11 * i) % 50 for i in range(300)]),
+]
+
+
+@pytest.mark.parametrize("name,hq,hkv,d,pb,own", SHARED_PREFIX_CASES,
+                         ids=[c[0] for c in SHARED_PREFIX_CASES])
+def test_shared_prefix_cases(name, hq, hkv, d, pb, own):
+    """Prefix lengths that end inside a 64-key tile and a chunk, rows past
+    one tile of sequences, one-block prefixes, every group size: all rows
+    against the oracle; two calls give identical bits."""
+    rows = [(1, 16 * pb + n - 1) for n in own]
+    spec = wl.custom(name, hq, hkv, d, rows=rows, seed=120 + pb, shared_prefix_blocks=pb)
+    banner(f"shared prefix {name}: S={spec.num_seqs} prefix={pb} blocks Hq={hq} Hkv={hkv} D={d}")
+    case = wl.make_case(spec, device=DEV)
+    out = shared_prefix_call(case, pb).clone()
+    out2 = pa.forward_shared_prefix(case.q, case.k_cache, case.v_cache, case.block_table,
+                                    case.seq_lens, case.query_start_loc, case.scale, pb,
+                                    max_seq_len=max(spec.seq_lens))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    seqs = list(range(spec.num_seqs))
+    if len(seqs) > 64:
+        seqs = seqs[:24] + seqs[-24:]
+    r, want = oracle_rows(case, seqs)
+    assert_close(out.cpu()[r], want, name)
+
+
+def test_shared_prefix_rejects_bad_arguments():
+    spec = wl.custom("sp_bad", 32, 8, 128, rows=[(1, 40), (1, 50)], seed=130,
+                     shared_prefix_blocks=2)
+    case = wl.make_case(spec, device=DEV)
+    args = (case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+            case.query_start_loc, case.scale)
+    with pytest.raises((ValueError, pa.PaError)):
+        pa.forward_shared_prefix(*args, 0)
+    with pytest.raises((ValueError, pa.PaError)):
+        pa.forward_shared_prefix(*args, 4, max_seq_len=51)  # prefix covers every key
+
+
+# ---------------------------------------------------------------------------
 # Sweep of shapes and edge cases (small enough for the full oracle)
 # ---------------------------------------------------------------------------
 
