@@ -262,7 +262,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["decode", "mixed", "long", "prefix", "tiny", "copy",
-                                       "mixed_decode", "mixed_prefill"], default=None)
+                                       "mixed_decode", "mixed_prefill", "spec_decode"],
+                    default=None)
     ap.add_argument("--all", action="store_true",
                     help="also time the long-decode, prefix-shared and tiny workloads")
     args = ap.parse_args(argv)
@@ -329,13 +330,15 @@ def main(argv=None):
                                kernels={k: round(v * 1e3, 3) for k, v in kmean_m.items()})
 
     others = []
-    if args.all or args.only in ("long", "prefix", "tiny", "mixed_decode", "mixed_prefill"):
+    if args.all or args.only in ("long", "prefix", "tiny", "mixed_decode", "mixed_prefill",
+                                 "spec_decode"):
         m3 = wl.config(3)
         for name, i, rot in (("long", 4, 1), ("prefix", 5, ROTATIONS), ("tiny", 1, 1),
-                             ("mixed_decode", 3, 1), ("mixed_prefill", 3, 1)):
+                             ("spec_decode", 6, 1), ("mixed_decode", 3, 1),
+                             ("mixed_prefill", 3, 1)):
             if args.only != name and (args.only is not None or name.startswith("mixed_")):
                 continue
-            spec = wl.config(i)
+            spec = wl.spec_decode(4) if name == "spec_decode" else wl.config(i)
             if name == "mixed_decode":
                 spec = sub_spec(m3, [s for s in range(m3.num_seqs) if m3.q_lens[s] == 1], name)
             if name == "mixed_prefill":
@@ -363,6 +366,15 @@ def main(argv=None):
                     "tokens_per_s": round(spec.num_tokens / (ms2 * 1e-3), 1)}
             if i == 4:
                 entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if name == "spec_decode":
+                entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                # the same rows without the tight hint: the prefill path
+                inp.hints["max_query_len"] = None
+                ms2, km2, _, fwd2 = run_steps(pa, inp, args.steps, args.warmup)
+                entry["prefill_path"] = {
+                    "ms_per_step": round(ms2, 5), "ms_forward_kernels": round(fwd2, 5),
+                    "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in km2.items()},
+                    "forward_gbs_logical": round(b / (fwd2 * 1e-3) / 1e9, 2)}
             others.append((name, entry))
             del inp
             torch.cuda.empty_cache()

@@ -93,12 +93,16 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
  * split between workgroups and the work list of prefill tiles. Depends only
  * on its arguments (and on the tuning overrides read once per process);
  * returns 0 if an argument is out of range or the sizes are not supported.
- * max_seq_len_hint <= 0 means "unknown" (max_blocks_per_seq * 16 is used).
+ * The hints are those the forward call will pass: max_query_len_hint with
+ * 1 < hint <= 16 / (num_q_heads / num_kv_heads) plans for rows of several
+ * query tokens on the decode path; max_seq_len_hint <= 0 means "unknown"
+ * (max_blocks_per_seq * 16 is used).
  */
 #define PA_WORKSPACE_COUNTER_BYTES (256u * 1024u)
 size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_size,
-                                  int32_t max_blocks_per_seq, int32_t max_seq_len_hint);
+                                  int32_t max_blocks_per_seq, int32_t max_query_len_hint,
+                                  int32_t max_seq_len_hint);
 
 /*
  * Paged attention over a flattened varlen batch (section "Run forward pass",
@@ -132,7 +136,11 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * Rows with q_len == 0 produce nothing; rows with q_len == 1 take the decode
  * path (for large batches the rows' blocks are shared out evenly between
  * workgroups; small batches, or more than 4096 rows, split rows into fixed
- * partitions), rows with q_len > 1 the prefill path.
+ * partitions), rows with q_len > 1 the prefill path. When 1 <
+ * max_query_len_hint <= 16 / (num_q_heads / num_kv_heads) (for instance
+ * rows verifying a few speculated tokens) every row takes the partitioned
+ * decode path, its q_len * G query columns sharing each K/V block, and no
+ * prefill launch is made.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
  * Tuning overrides, read once per process (for sweeps; out-of-range values
  * are ignored): PA_DECODE_STREAM (0 / 1 = always the partitioned / the

@@ -45,7 +45,7 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPO
 SIGNATURES = {
     "pa_kv_block_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "pa_cache_write": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P]),
-    "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_shared_prefix_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pa_forward_shared_prefix": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
                                                 _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
@@ -160,9 +160,13 @@ def cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 
 def forward_workspace_bytes(num_tokens: int, num_seqs: int, num_q_heads: int, num_kv_heads: int,
                             head_size: int, max_blocks_per_seq: int,
-                            max_seq_len: Optional[int] = None) -> int:
+                            max_seq_len: Optional[int] = None,
+                            max_query_len: Optional[int] = None) -> int:
+    """Workspace bytes of a forward call with these sizes and hints (the
+    same hints the call passes)."""
     n = load_library().pa_forward_workspace_bytes(num_tokens, num_seqs, num_q_heads, num_kv_heads,
-                                                  head_size, max_blocks_per_seq, max_seq_len or 0)
+                                                  head_size, max_blocks_per_seq,
+                                                  max_query_len or 0, max_seq_len or 0)
     if n == 0:
         raise ValueError("unsupported sizes for pa_forward")
     return int(n)
@@ -211,7 +215,8 @@ def _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, s
         if decode_schedule not in _SCHEDULE_FLAGS:
             raise ValueError(f"decode_schedule must be one of {sorted(_SCHEDULE_FLAGS)}")
         flags |= _SCHEDULE_FLAGS[decode_schedule]
-    need = lib.pa_forward_workspace_bytes(T, S, Hq, Hkv, D, MB, max_seq_len or 0)
+    need = lib.pa_forward_workspace_bytes(T, S, Hq, Hkv, D, MB, max_query_len or 0,
+                                          max_seq_len or 0)
     if workspace is None:
         workspace = _workspace(q.device, need)
     elif workspace.device != q.device:

@@ -112,11 +112,14 @@ struct WaveAcc {
 };
 
 // Q^T as the B operand: lane holds query column hl (< ncols, else zeros),
-// d = 32*i + 8*grp + e.
+// d = 32*i + 8*grp + e. Column hl is head hl % G of token hl / G of the row
+// (qrow: the row's first token, its KV head's first query head; Hq heads
+// per token).
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qv)[D / 32], const uint16_t* __restrict__ qrow,
-                                       int hl, int grp, int ncols) {
-  const u32x4* qp = (const u32x4*)(qrow + (int64_t)hl * D) + grp;
+                                       int hl, int grp, int ncols, int G, int Hq) {
+  const int col = hl < ncols ? hl : 0;
+  const u32x4* qp = (const u32x4*)(qrow + ((int64_t)(col / G) * Hq + col % G) * D) + grp;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -135,16 +138,20 @@ struct NewToken {
 
 // Streams nk (1..64) blocks of one KV head into acc: block k's id sits in lane
 // k of `ids`, its first token is tok0 + k * tok_step, and tokens >= tok_end
-// are masked (their V rows zeroed). kbase / vbase point at the head's slice
-// of block 0 (kbase already offset to the lane's K row and chunk); vl is the
-// wave's LDS slice. With kNew, token nt.tok is read from nt.k / nt.v.
+// are masked (their V rows zeroed). col_lim (per lane: its query column's
+// last visible key, >= tok_end - 1 for a single-token row) masks the tail
+// of a row with several query tokens causally. kbase / vbase point at the
+// head's slice of block 0 (kbase already offset to the lane's K row and
+// chunk); vl is the wave's LDS slice. With kNew, token nt.tok is read from
+// nt.k / nt.v.
 template <int D, int NBUF, bool kStreamV, bool kNew = false>
 __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv)[D / 32], int ids,
                                               int nk, int tok0, int tok_step, int tok_end,
                                               const uint16_t* __restrict__ kbase,
                                               const uint16_t* __restrict__ vbase, int64_t kv_row,
                                               uint16_t* vl, float scale_log2, int lane,
-                                              NewToken nt = NewToken{-1, nullptr, nullptr}) {
+                                              NewToken nt = NewToken{-1, nullptr, nullptr},
+                                              int col_lim = INT32_MAX) {
   using Sh = DecodeShape<D>;
   const int hl = lane & 15;
   const int grp = lane >> 4;
@@ -197,14 +204,16 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tok = tokb + 4 * grp + r;
-      sv[r] = tok < tok_end ? sacc[r] * scale_log2 : -INFINITY;
+      sv[r] = (tok < tok_end && tok <= col_lim) ? sacc[r] * scale_log2 : -INFINITY;
       over |= sv[r] > acc.m + kLazy;
     }
     if (__any(over)) {  // wave-uniform: re-reference the softmax
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       bm = max_across_groups(bm);
       const float mn = fmaxf(acc.m, bm);
-      const float alpha = fast_exp2(acc.m - mn);
+      // (o and the sum are still zero while m is -inf: a column that has
+      // seen no visible key keeps m = -inf without a NaN)
+      const float alpha = acc.m == -INFINITY ? 0.f : fast_exp2(acc.m - mn);
       acc.lsum *= alpha;
 #pragma unroll
       for (int mi = 0; mi < Sh::kDTiles; ++mi) acc.o[mi] *= alpha;
@@ -213,7 +222,9 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = fast_exp2(sv[r] - acc.m);
+      // (a column of a several-token row can meet a block with none of its
+      // keys visible before any visible one: m is still -inf there)
+      p[r] = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - acc.m);
       acc.lsum += p[r];
     }
     const u32x2 s01 = split_pack_bf16x2(p[0], p[1]);
@@ -294,7 +305,9 @@ __device__ __forceinline__ void merge_waves(const WaveAcc<D>& acc, float* stage,
       for (int sub = 0; sub < S; ++sub) {
         const int v = slot + HG * sub;
         const float* ml = mml + (v * Sh::kMergeCols + h) * 2;
-        const float e = fast_exp2(ml[0] - M);
+        // a column that saw no visible key (m = -inf) adds nothing, also
+        // when no wave saw one (M = -inf)
+        const float e = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
         const float* orow = mo + (v * Sh::kMergeCols + h) * Sh::kMergeRow + d;
         den += e * ml[1];
         n0 += e * orow[0];
@@ -430,7 +443,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
     const int nk_all = (j_hi - j_lo > sub) ? (j_hi - j_lo - 1 - sub) / Ssub + 1 : 0;
     if (head_ok && nk_all > 0) {
       bf16x8 qv[Sh::kKChunks];
-      load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G);
+      load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G, G, Hq);
       const uint16_t* kbase = k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row;
       const uint16_t* vbase = v_cache + (int64_t)g * D;
       const int32_t* trow = block_table + (int64_t)s * MB + j_lo + sub;
@@ -531,7 +544,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     float scale_log2, int32_t Hq, int32_t Hkv, int32_t G, int32_t MB, int32_t part_tokens,
-    int32_t num_parts_max, int32_t tok_base, int32_t part_base,
+    int32_t num_parts_max, int32_t tok_base, int32_t part_base, int32_t QM,
     const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
     const int64_t* __restrict__ slot_mapping, uint16_t* k_cache_w, uint16_t* v_cache_w) {
   using Sh = DecodeShape<D>;
@@ -558,8 +571,13 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   const int my_blk = (jb < bpp && b_begin + jb < MB)
                          ? block_table[(int64_t)s * MB + b_begin + jb] : 0;
   // Workgroup-uniform exits (before any barrier).
+  // Rows of 1..QM query tokens: token i of the row sits at position
+  // L - ql + i and sees keys up to it; the row's ql * G (<= 16) query
+  // columns share every K/V block.
   const int t0 = qsl[s];
-  if (qsl[s + 1] - t0 != 1) return;  // not a decode row
+  const int ql = qsl[s + 1] - t0;
+  if (ql < 1 || ql > QM) return;  // not a decode row
+  const int ncols = ql * G;
   const int L = seq_lens[s];
   const int tok_begin = tok_base + part * part_tokens;
   if (tok_begin >= L) return;
@@ -591,43 +609,52 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   acc.init();
   if (nmine > 0) {
     bf16x8 qv[Sh::kKChunks];
-    load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G);
+    load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
+    const int col_lim = L - ql + min(hl, ncols - 1) / G;  // last key of the lane's column
     stream_blocks<D, NBUF, kStreamV, kWrite>(
         acc, qv, my_blk, nmine, (b_begin + w) * kBlock, W * kBlock, tok_end,
         k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row, v_cache + (int64_t)g * D,
-        kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt);
+        kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt, col_lim);
     acc.lsum = sum_across_groups(acc.lsum);
   }
 
-  merge_waves<D>(acc, (float*)lds, W, 1, G, w, lane,
+  merge_waves<D>(acc, (float*)lds, W, 1, ncols, w, lane,
                  [&](int, int col, int d, float M, float den, float n0, float n1) {
-    const int qh = g * G + col;
+    const int tk = col / G;
+    const int qh = g * G + col % G;
     if (nparts == 1 && part_base == 0) {
       const float inv = 1.0f / den;
-      *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+      *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) =
+          pack_bf16x2(n0 * inv, n1 * inv);
     } else {  // read by the combine kernel after this one ends
-      const int64_t base = ((int64_t)s * num_parts_max + part_base + part) * Hq + qh;
+      const int64_t base =
+          (((int64_t)s * num_parts_max + part_base + part) * QM + tk) * Hq + qh;
       *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
       if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
     }
   });
 }
 
-// Merge of a row's partitions: one wave per (row, head), lanes across d,
-// partitions in order (deterministic). Rows vary fastest in the grid.
+// Merge of a row's partitions: one wave per (row, query token, head), lanes
+// across d, partitions in order (deterministic). Rows vary fastest in the
+// grid. Partial p of token tk sits at ((s * num_parts_max + p) * QM + tk)
+// * Hq + head.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml, uint16_t* __restrict__ out,
     int32_t Hq, int32_t part_tokens, int32_t num_parts_max, int32_t tok_base,
-    int32_t part_base) {
+    int32_t part_base, int32_t QM) {
   constexpr int kPer = D / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int s = blockIdx.x;
-  const int qh = blockIdx.y * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (qh >= Hq) return;
+  const int idx = blockIdx.y * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int tk = idx / Hq;
+  const int qh = idx - tk * Hq;
+  if (tk >= QM) return;
   const int t0 = qsl[s];
-  if (qsl[s + 1] - t0 != 1) return;
+  const int ql = qsl[s + 1] - t0;
+  if (ql < 1 || ql > QM || tk >= ql) return;
   const int L = seq_lens[s];
   // partials 0 .. part_base-1 come from the shared-prefix pass
   // (clamped to the workspace rows: a length past the planned maximum is a
@@ -635,12 +662,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   const int np =
       min(num_parts_max, part_base + max(0, (L - tok_base + part_tokens - 1) / part_tokens));
   if (np <= 1) return;
-  const int64_t row0 = (int64_t)s * num_parts_max * Hq + qh;  // partition p at row0 + p*Hq
+  const int64_t pstride = (int64_t)QM * Hq;  // partition p at row0 + p * pstride
+  const int64_t row0 = (int64_t)s * num_parts_max * pstride + (int64_t)tk * Hq + qh;
 
   float M = -INFINITY;
   for (int p0 = 0; p0 < np; p0 += kWave) {
     const int p = p0 + lane;
-    if (p < np) M = fmaxf(M, ws_ml[(row0 + (int64_t)p * Hq) * 2]);
+    if (p < np) M = fmaxf(M, ws_ml[(row0 + p * pstride) * 2]);
   }
   M = wave_max(M);
 
@@ -652,8 +680,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
     const int p = p0 + lane;
     float wgt = 0.f;
     if (p < np) {
-      const int64_t r = row0 + (int64_t)p * Hq;
-      wgt = fast_exp2(ws_ml[r * 2] - M);
+      const int64_t r = row0 + p * pstride;
+      wgt = ws_ml[r * 2] == -INFINITY ? 0.f : fast_exp2(ws_ml[r * 2] - M);
       wl += wgt * ws_ml[r * 2 + 1];
     }
     const int cnt = min(kWave, np - p0);
@@ -663,7 +691,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int kk = min(k0 + k, cnt - 1);
-        const float* op = ws_o + (row0 + (int64_t)(p0 + kk) * Hq) * D;
+        const float* op = ws_o + (row0 + (p0 + kk) * pstride) * D;
 #pragma unroll
         for (int e = 0; e < kPer; ++e) vals[k][e] = op[lane + kWave * e];
       }
@@ -679,7 +707,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   }
   const float W = wave_sum(wl);
   const float inv = 1.0f / W;
-  uint16_t* op = out + ((int64_t)t0 * Hq + qh) * D;
+  uint16_t* op = out + ((int64_t)(t0 + tk) * Hq + qh) * D;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) op[lane + kWave * e] = float_to_bf16_bits(acc[e] * inv);
 }
@@ -713,7 +741,8 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       p.tok_base, p.part_base, (const uint16_t*)p.knew, (const uint16_t*)p.vnew,
+                       p.tok_base, p.part_base, p.qmax, (const uint16_t*)p.knew,
+                       (const uint16_t*)p.vnew,
                        p.slot_mapping, (uint16_t*)p.k_cache_w, (uint16_t*)p.v_cache_w);
   } else {
     hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, false>), grid, dim3(p.waves * kWave),
@@ -721,16 +750,17 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       p.tok_base, p.part_base, nullptr, nullptr, nullptr, nullptr, nullptr);
+                       p.tok_base, p.part_base, p.qmax, nullptr, nullptr, nullptr, nullptr,
+                       nullptr);
   }
   profile_end(PA_KERNEL_DECODE, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.num_parts_max <= 1) return e;
-  dim3 cgrid(a.num_seqs, (a.num_q_heads + 3) / 4);
+  dim3 cgrid(a.num_seqs, (p.qmax * a.num_q_heads + 3) / 4);
   profile_begin(PA_KERNEL_COMBINE, stream);
   hipLaunchKernelGGL(decode_combine_kernel<D>, cgrid, dim3(256), 0, stream, a.seq_lens,
                      a.query_start_loc, p.ws_o, p.ws_ml, (uint16_t*)a.out, a.num_q_heads,
-                     p.part_tokens, p.num_parts_max, p.tok_base, p.part_base);
+                     p.part_tokens, p.num_parts_max, p.tok_base, p.part_base, p.qmax);
   profile_end(PA_KERNEL_COMBINE, stream);
   return hipGetLastError();
 }
@@ -758,6 +788,9 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
     return hipErrorInvalidValue;
   if (p.tok_base < 0 || p.tok_base % kBlock || p.part_base < 0 ||
       p.num_parts_max - p.part_base < 1 || ((p.tok_base || p.part_base) && p.stream))
+    return hipErrorInvalidValue;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (p.qmax < 1 || p.qmax * G > 16 || (p.qmax > 1 && (p.stream || p.fused_write)))
     return hipErrorInvalidValue;
   if (p.stream) {
     if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||

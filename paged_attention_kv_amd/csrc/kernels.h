@@ -55,6 +55,9 @@ struct DecodePlan {
   // leaves partials for the combine (even with one partition).
   int32_t tok_base;
   int32_t part_base;
+  // Partitioned schedule: rows of 1..qmax query tokens (qmax * G <= 16)
+  // take the decode path; partials are laid out per query token.
+  int32_t qmax;
   // Fused write (partitioned schedule, decode rows only): the decode launch
   // also writes each row's new token and reads it from knew / vnew.
   bool fused_write;
@@ -105,12 +108,13 @@ hipError_t launch_prefix(const ForwardArgs& a, const PrefixPlan& p, hipStream_t 
 // Workspace layout shared by pa_forward and pa_forward_workspace_bytes.
 struct WorkspaceLayout {
   bool stream_ok, stream_default;  // even shares fit / are the default schedule
+  int32_t qmax;                    // query tokens per decode row (see DecodePlan)
   int32_t stream_wgs, stream_heads, stream_waves, waves, prefetch;
   int32_t part_tokens, num_parts_max, tile_queries, bound_a, bound_b;
   size_t off_ctr, off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;
 };
 bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,
-                    int32_t max_seq_len_hint, WorkspaceLayout* out);
+                    int32_t max_query_len_hint, int32_t max_seq_len_hint, WorkspaceLayout* out);
 
 }  // namespace pa

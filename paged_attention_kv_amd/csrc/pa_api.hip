@@ -106,6 +106,14 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t waves
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
+// Query tokens per row that the decode kernel takes (rows of 1..qmax
+// tokens, their qmax * G columns in one 16-column matrix tile): with a host
+// bound 1 < max_query_len_hint <= 16 / G every row runs there and no prefill
+// launch is made; otherwise single-token rows only.
+int32_t decode_qmax(int32_t group, int32_t max_query_len_hint) {
+  return (max_query_len_hint > 1 && max_query_len_hint * group <= 16) ? max_query_len_hint : 1;
+}
+
 // Decode schedules. Even shares (the stream kernel: equal shares of all
 // rows' blocks per workgroup) fit when the batch has few enough rows for the
 // per-workgroup row scan; they are the default when shares would be long
@@ -146,7 +154,7 @@ namespace pa {
 
 bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,
-                    int32_t max_seq_len_hint, WorkspaceLayout* out) {
+                    int32_t max_query_len_hint, int32_t max_seq_len_hint, WorkspaceLayout* out) {
   if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_size <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads)
     return false;
@@ -154,6 +162,7 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   if (!supported_group(group)) return false;
   const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
   WorkspaceLayout w;
+  w.qmax = decode_qmax(group, max_query_len_hint);
   w.prefetch = decode_prefetch(head_size);
   // Both decode schedules' parameters; the partial results region fits
   // either, so a per-call flag may pick one.
@@ -168,7 +177,7 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   if (w.num_parts_max > kMaxGridZ) return false;
   const size_t stream_rows = w.stream_ok ? (size_t)w.stream_wgs * 2 * num_q_heads : 0;
   const size_t part_rows =
-      w.num_parts_max > 1 ? (size_t)num_seqs * w.num_parts_max * num_q_heads : 0;
+      w.num_parts_max > 1 ? (size_t)num_seqs * w.num_parts_max * w.qmax * num_q_heads : 0;
   const size_t rows = std::max(stream_rows, part_rows);  // (share, slot, head) / (row, part, head)
   const size_t dec_o = rows * head_size, dec_ml = rows * 2;
   w.tile_queries = prefill_tile_queries(group);
@@ -226,10 +235,11 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
 
 size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_size,
-                                  int32_t max_blocks_per_seq, int32_t max_seq_len_hint) {
+                                  int32_t max_blocks_per_seq, int32_t max_query_len_hint,
+                                  int32_t max_seq_len_hint) {
   pa::WorkspaceLayout w;
   if (!pa::plan_workspace(num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
-                          max_blocks_per_seq, max_seq_len_hint, &w))
+                          max_blocks_per_seq, max_query_len_hint, max_seq_len_hint, &w))
     return 0;
   return w.total;
 }
@@ -306,7 +316,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     return fail(PA_ERR_ALIGN, "pa_forward: q, caches and out must be 16-byte aligned");
   pa::WorkspaceLayout w;
   if (!pa::plan_workspace(num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
-                          max_blocks_per_seq, max_seq_len_hint, &w))
+                          max_blocks_per_seq, max_query_len_hint, max_seq_len_hint, &w))
     return fail(PA_ERR_SHAPE, "pa_forward: cannot plan the workspace");
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_ERR_WORKSPACE, "pa_forward: workspace of %zu bytes, %zu needed",
@@ -336,9 +346,10 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   char* ws = (char*)workspace;
 
   pa::DecodePlan dp;
-  dp.stream = (flags & PA_FORWARD_DECODE_EVEN_SHARES)  ? w.stream_ok
-              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
-                                                        : w.stream_default;
+  dp.stream = w.qmax == 1 && ((flags & PA_FORWARD_DECODE_EVEN_SHARES)    ? w.stream_ok
+                              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
+                                                                        : w.stream_default);
+  dp.qmax = w.qmax;
   const bool fused = wr && max_query_len_hint == 1 && !dp.stream;
   if (wr && !fused) {
     hipError_t e = pa::launch_cache_write(wr->k, wr->v, wr->slot_mapping, wr->k_cache,
@@ -346,7 +357,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward cache write launch");
   }
 
-  if (a.max_query_len > 1) {
+  if (a.max_query_len > w.qmax) {
     pa::PrefillPlan pp;
     pp.tile_queries = w.tile_queries;
     pp.split_tile_queries = pa::prefill_split_tile_queries(num_q_heads / num_kv_heads);
@@ -584,6 +595,7 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   dp.ws_ml = pp.ws_ml;
   dp.tok_base = pl.prefix_keys;
   dp.part_base = pl.chunks;
+  dp.qmax = 1;
   e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix decode launch");
   return PA_OK;

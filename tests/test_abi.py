@@ -124,6 +124,32 @@ def test_workspace_sizes_for_the_named_workloads(lib, i):
     assert n2 <= n
 
 
+def test_workspace_for_multi_token_decode_rows(lib):
+    # a hint of 4 query tokens per row at 4 query heads per KV head plans the
+    # decode partials per query token (up to 4x); a hint past 16 / G does not
+    args = (1024, 256, 32, 8, 128, 512)
+    n1 = pa.forward_workspace_bytes(*args, 8192, max_query_len=1)
+    n4 = pa.forward_workspace_bytes(*args, 8192, max_query_len=4)
+    n5 = pa.forward_workspace_bytes(*args, 8192, max_query_len=5)
+    assert n1 < n4 <= 4 * n1 and n5 <= n4
+
+
+def test_shared_prefix_workspace(lib):
+    s = wl.config(5)
+    n = lib.pa_shared_prefix_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads,
+                                             s.head_size, s.max_blocks_per_seq,
+                                             s.shared_prefix_blocks, max(s.seq_lens))
+    # partials: at least one chunk and the row's own blocks per row and head
+    assert n >= s.num_seqs * 2 * s.num_q_heads * (s.head_size + 2) * 4
+    assert n % 256 == 0
+    # the prefix must leave keys for every row, and be at least one block
+    assert lib.pa_shared_prefix_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads,
+                                                s.head_size, s.max_blocks_per_seq, 0, 0) == 0
+    assert lib.pa_shared_prefix_workspace_bytes(s.num_seqs, s.num_q_heads, s.num_kv_heads,
+                                                s.head_size, s.max_blocks_per_seq,
+                                                s.max_blocks_per_seq, 0) == 0
+
+
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define PA_BLOCK_SIZE (\d+)", text).group(1)) == pa.BLOCK_SIZE

@@ -173,6 +173,63 @@ def test_prefix_shared_sampled_rows(shared_flag):
 
 
 # ---------------------------------------------------------------------------
+# Rows of a few query tokens on the decode path (speculative verify)
+# ---------------------------------------------------------------------------
+
+MULTI_TOKEN_CASES = [
+    # name, Hq, Hkv, D, rows (q_len, prior context)
+    ("g4_d128", 32, 8, 128, [(4, 300), (3, 0), (1, 77), (2, 127), (4, 4093), (0, 5), (4, 124),
+                            (4, 1), (3, 2500)]),
+    ("g8_d64", 64, 8, 64, [(2, 0), (1, 1000), (2, 513), (2, 4094), (2, 15), (1, 0)]),
+    ("g1_d128", 8, 8, 128, [(16, 0), (16, 200), (9, 3000), (1, 50), (13, 115)]),
+    ("g2_d64", 16, 8, 64, [(8, 1), (7, 640), (8, 9000), (3, 33)]),
+]
+
+
+@pytest.mark.parametrize("hinted", [True, False])
+@pytest.mark.parametrize("name,hq,hkv,d,rows", MULTI_TOKEN_CASES,
+                         ids=[c[0] for c in MULTI_TOKEN_CASES])
+def test_multi_token_decode_rows(name, hq, hkv, d, rows, hinted):
+    """Rows of up to 16 / G query tokens: with the tight max_query_len hint
+    they run on the decode path (no prefill launch), without it on the
+    prefill path; both match the oracle on every row (causal tail inside
+    the last blocks, rows with no prior context, rows split into several
+    partitions)."""
+    spec = wl.custom(name, hq, hkv, d, rows=rows, seed=140 + len(rows))
+    banner(f"multi-token decode rows {name}: hinted={hinted} q_lens={spec.q_lens}")
+    case = wl.make_case(spec, device=DEV)
+    pa.profile_begin()
+    out = write_and_forward(case, hints=hinted)
+    per = pa.profile_end()
+    if hinted:
+        assert "prefill" not in per and "plan" not in per, per
+    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
+    r, want = oracle_rows(case, seqs)
+    assert_close(out.cpu()[r], want, name)
+
+
+def test_multi_token_decode_rows_nan_poison_and_schedules():
+    """NaN in every cache row outside the contexts; rows of 4 tokens split
+    into many partitions, against the oracle."""
+    rows = [(4, 9000), (4, 100), (4, 3), (2, 4000)]
+    spec = wl.custom("mt_nan", 32, 8, 128, rows=rows, seed=150)
+    case = wl.make_case(spec, device=DEV, poison=float("nan"))
+    out = write_and_forward(case, hints=True, decode_schedule="partitioned")
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "nan poison")
+
+
+def test_spec_decode_workload_sampled_rows():
+    spec = wl.spec_decode(4)
+    banner("speculative-verify workload: 256 rows x 4 query tokens")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case).cpu()
+    pick = sorted(random.Random(16).sample(range(256), 10) + [0, 255])
+    r, want = oracle_rows(case, pick)
+    assert_close(out[r], want, "spec decode")
+
+
+# ---------------------------------------------------------------------------
 # Shared-prefix decode (prefix attended once for all rows)
 # ---------------------------------------------------------------------------
 

@@ -136,6 +136,19 @@ def config(i: int) -> Spec:
     raise ValueError(f"no workload {i}")
 
 
+def spec_decode(q_len: int = 4) -> Spec:
+    """Rows verifying speculated tokens: 256 rows of q_len query tokens each,
+    prior contexts drawn like the mixed step's decode rows (U[256, 8192]),
+    32q/8kv, D128, 150k-block pool."""
+    g = torch.Generator().manual_seed(SEED_LAYOUT_BASE + 6)
+    ctx = _uniform(g, 256, 8192, 256)
+    return Spec("spec_decode", 32, 8, 128, num_blocks=150_000, max_blocks_per_seq=520,
+                q_lens=(q_len,) * 256, seq_lens=tuple(c + q_len for c in ctx),
+                description=(f"256 rows of {q_len} query tokens (speculative verify), prior "
+                             "context U[256,8192]; 32q/8kv, D128; 150k-block pool"),
+                seed_layout=SEED_LAYOUT_BASE + 6, seed_values=SEED_VALUES_BASE + 6)
+
+
 def custom(name: str, num_q_heads: int, num_kv_heads: int, head_size: int,
            rows: Sequence[Tuple[int, int]], seed: int, num_blocks: Optional[int] = None,
            max_blocks_per_seq: Optional[int] = None, shared_prefix_blocks: int = 0) -> Spec:
