@@ -42,7 +42,27 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPO
           -7: "PA_ERR_INVALID_DATA"}
 
 # (name, restype, argtypes) of every symbol include/pa.h declares.
+class SchedStats(ctypes.Structure):
+    """pa_sched_stats (include/pa_sched.h)."""
+    _fields_ = [("num_free_blocks", ctypes.c_int64), ("num_cached_blocks", ctypes.c_int64),
+                ("num_waiting", ctypes.c_int32), ("num_running", ctypes.c_int32),
+                ("num_finished", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("num_steps", ctypes.c_int64), ("prefix_hit_tokens", ctypes.c_int64),
+                ("num_preemptions", ctypes.c_int64)]
+
+
 SIGNATURES = {
+    "pa_sched_create": (_P, [_I64, _I32, _I32, _I32, _I32, _I32]),
+    "pa_sched_destroy": (None, [_P]),
+    "pa_sched_add_request": (ctypes.c_int, [_P, _I64, _P, _I32, _I32]),
+    "pa_sched_schedule": (ctypes.c_int, [_P, _P, _P, _P]),
+    "pa_sched_step_inputs": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _P, _P]),
+    "pa_sched_update": (ctypes.c_int, [_P, _P]),
+    "pa_sched_finish_request": (ctypes.c_int, [_P, _I64]),
+    "pa_sched_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(SchedStats)]),
+    "pa_sched_request_blocks": (_I32, [_P, _I64, _P, _I32]),
+    "pa_sched_request_computed": (_I32, [_P, _I64]),
+    "pa_sched_block_ref_count": (_I32, [_P, _I32]),
     "pa_kv_block_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "pa_cache_write": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P]),
     "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),

@@ -1,5 +1,6 @@
-"""Build step of the HIP library: compiles every ``csrc/*.hip`` for gfx950 and
-links ``libpa.so`` next to this file. Run ``python -m paged_attention_kv_amd.build``
+"""Build step of the HIP library: compiles every ``csrc/*.hip`` for gfx950
+(and the host-only ``csrc/*.cpp`` with the host compiler) and links
+``libpa.so`` next to this file. Run ``python -m paged_attention_kv_amd.build``
 (or ``__graft_entry__.build()``)."""
 
 from __future__ import annotations
@@ -33,8 +34,13 @@ def hipcc() -> str:
     return path
 
 
+# Host-only sources (the block manager / step planner) build with the host
+# compiler.
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
 def sources() -> list[str]:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
@@ -44,7 +50,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [shutil.which("g++") or "g++", *HOST_FLAGS, "-c", src, "-o", obj]
+        else:
+            cmd = [cc, *FLAGS, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -11,6 +11,7 @@
 #include <unordered_set>
 #include <vector>
 
+#include "errors.h"
 #include "kernels.h"
 #include "pa.h"
 
@@ -27,6 +28,23 @@ int fail(int code, const char* fmt, ...) {
   g_last_error = buf;
   return code;
 }
+
+}  // namespace
+
+namespace pa {
+int record_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+void clear_error() { g_last_error.clear(); }
+}  // namespace pa
+
+namespace {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

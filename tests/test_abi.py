@@ -1,4 +1,4 @@
-"""The C ABI on the CPU: libpa.so loads, exports every symbol include/pa.h
+"""The C ABI on the CPU: libpa.so loads, exports every symbol include/*.h
 declares, and rejects bad host arguments before launching anything. No
 kernel runs here (no GPU), only host-side argument checks and pure host
 arithmetic."""
@@ -15,15 +15,19 @@ import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 NULL = None
 FAKE = 4096 * 16  # 16-byte aligned, never dereferenced: every call below fails before a launch
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
