@@ -183,6 +183,39 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool 
     return ms_step, mean, count, ms_fwd
 
 
+def run_graph_steps(pa, inp: StepInputs, steps: int, warmup: int) -> float:
+    """The same steps captured once per block-table set in a HIP graph
+    (torch.cuda.CUDAGraph over the library's launches) and replayed in turn;
+    returns ms per step (HIP events around the replays on the current
+    stream)."""
+    spec = inp.spec
+    graphs = []
+    for r in range(inp.rotations):
+        st = inp.sets[r]
+
+        def step(st=st):
+            pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
+                                 st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
+                                 out=st["out"], **inp.hints)
+        step()  # kernels loaded and the workspace allocated outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def sub_spec(spec, rows, name):
     """The same rows as a workload of their own (for attributing time)."""
     return wl.Spec(name, spec.num_q_heads, spec.num_kv_heads, spec.head_size,
@@ -297,12 +330,14 @@ def main(argv=None):
         b_attn = attention_bytes(spec)
         b_step = b_attn + write_bytes(spec)
         gbs = b_step / (ms_step * 1e-3) / 1e9
+        ms_graph = run_graph_steps(pa, inp, args.steps, args.warmup)
         ms_dec = kmean["decode"]
         fused = "cache_write" not in kcount  # the decode launch also wrote the new tokens
         b_dec = b_step if fused else b_attn
         result["decode"] = dict(ms_step=ms_step, gbs=gbs, ms_fwd=ms_fwd, ms_decode_kernel=ms_dec,
                                 kernel_gbs=b_dec / (ms_dec * 1e-3) / 1e9, bytes_step=b_step,
                                 bytes_fwd=b_dec, fused=fused, rotations=inp.rotations,
+                                ms_graph=ms_graph,
                                 kernels={k: round(v * 1e3, 3) for k, v in kmean.items()})
         del inp
         torch.cuda.empty_cache()
@@ -390,6 +425,10 @@ def main(argv=None):
                          "32 q / 4 kv heads, head_size 64, block 16, 100k-block bf16 pool; "
                          "KV write + paged attention"),
             "tokens": 64, "kv_bytes_per_step": d["bytes_step"],
+            "graph_replay": {"ms_per_step": round(d["ms_graph"], 5),
+                             "gbs": round(d["bytes_step"] / (d["ms_graph"] * 1e-3) / 1e9, 2),
+                             "note": "the same step captured in a HIP graph per block-table "
+                                     "set and replayed (value uses eager launches)"},
             "block_table_rotations": d["rotations"],
             "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
         kname = "decode_kernel<64, 2, true, %s>" % ("true" if d["fused"] else "false")
