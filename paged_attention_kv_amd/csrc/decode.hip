@@ -545,8 +545,9 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     float scale_log2, int32_t Hq, int32_t Hkv, int32_t G, int32_t MB, int32_t part_tokens,
     int32_t num_parts_max, int32_t tok_base, int32_t part_base, int32_t QM,
-    const uint16_t* __restrict__ knew, const uint16_t* __restrict__ vnew,
-    const int64_t* __restrict__ slot_mapping, uint16_t* k_cache_w, uint16_t* v_cache_w) {
+    int32_t* __restrict__ counters, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, const int64_t* __restrict__ slot_mapping,
+    uint16_t* k_cache_w, uint16_t* v_cache_w) {
   using Sh = DecodeShape<D>;
   // W V slices of kLdsWave elements while streaming; the merge stage after.
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -618,21 +619,83 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
     acc.lsum = sum_across_groups(acc.lsum);
   }
 
+  // With counters, the workgroup that finishes a split row last merges its
+  // partials (no combine launch): partials go past this XCD's L2.
+  const bool split = nparts > 1 || part_base > 0;
   merge_waves<D>(acc, (float*)lds, W, 1, ncols, w, lane,
                  [&](int, int col, int d, float M, float den, float n0, float n1) {
     const int tk = col / G;
     const int qh = g * G + col % G;
-    if (nparts == 1 && part_base == 0) {
+    if (!split) {
       const float inv = 1.0f / den;
       *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) =
           pack_bf16x2(n0 * inv, n1 * inv);
-    } else {  // read by the combine kernel after this one ends
+    } else {
       const int64_t base =
           (((int64_t)s * num_parts_max + part_base + part) * QM + tk) * Hq + qh;
-      *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
-      if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
+      if (counters) {
+        store_coherent2(ws_o + base * D + d, n0, n1);
+        if (d == 0) store_coherent2(ws_ml + base * 2, M, den);
+      } else {  // read by the combine kernel after this one ends
+        *(f32x2*)(ws_o + base * D + d) = f32x2{n0, n1};
+        if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
+      }
     }
   });
+  if (!counters || !split) return;
+  // Publish: this workgroup's partial stores have completed before it counts
+  // itself in; the last of the row's nparts workgroups (of this KV head)
+  // merges partials 0 .. part_base + nparts - 1 in order and leaves the
+  // counter at zero for the next call.
+  int32_t* flag = (int32_t*)lds;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // (partitions past the grid do not run: a length past the planned
+  // maximum is a caller error, and the counter still returns to zero)
+  const int nrun = min(nparts, (int)gridDim.z);
+  if (threadIdx.x == 0) {
+    int32_t* ctr = counters + (int64_t)s * Hkv + g;
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == nrun - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  const int np = part_base + nrun;
+  const int64_t pstride = (int64_t)QM * Hq;
+  for (int idx = threadIdx.x; idx < ncols * (D / 2); idx += blockDim.x) {
+    const int col = idx / (D / 2);
+    const int d = 2 * (idx % (D / 2));
+    const int tk = col / G;
+    const int qh = g * G + col % G;
+    const int64_t row0 = (int64_t)s * num_parts_max * pstride + (int64_t)tk * Hq + qh;
+    float M = -INFINITY, den = 0.f, n0 = 0.f, n1 = 0.f;
+    for (int c0 = 0; c0 < np; c0 += 8) {
+      f32x2 ml[8], ov[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t r = row0 + min(c0 + k, np - 1) * pstride;
+        ml[k] = load_coherent2(ws_ml + r * 2);
+        ov[k] = load_coherent2(ws_o + r * D + d);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // a partition where the column saw no visible key adds nothing
+        if (c0 + k < np && ml[k][0] != -INFINITY) {
+          const float mn = fmaxf(M, ml[k][0]);
+          const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+          const float e = fast_exp2(ml[k][0] - mn);
+          den = den * sc + e * ml[k][1];
+          n0 = n0 * sc + e * ov[k][0];
+          n1 = n1 * sc + e * ov[k][1];
+          M = mn;
+        }
+      }
+    }
+    const float inv = 1.0f / den;
+    *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+  }
 }
 
 // Merge of a row's partitions: one wave per (row, query token, head), lanes
@@ -741,7 +804,8 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       p.tok_base, p.part_base, p.qmax, (const uint16_t*)p.knew,
+                       p.tok_base, p.part_base, p.qmax,
+                       p.fused_combine ? p.counters : nullptr, (const uint16_t*)p.knew,
                        (const uint16_t*)p.vnew,
                        p.slot_mapping, (uint16_t*)p.k_cache_w, (uint16_t*)p.v_cache_w);
   } else {
@@ -750,12 +814,13 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       p.tok_base, p.part_base, p.qmax, nullptr, nullptr, nullptr, nullptr,
-                       nullptr);
+                       p.tok_base, p.part_base, p.qmax,
+                       p.fused_combine ? p.counters : nullptr, nullptr, nullptr, nullptr,
+                       nullptr, nullptr);
   }
   profile_end(PA_KERNEL_DECODE, stream);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.num_parts_max <= 1) return e;
+  if (e != hipSuccess || p.num_parts_max <= 1 || p.fused_combine) return e;
   dim3 cgrid(a.num_seqs, (p.qmax * a.num_q_heads + 3) / 4);
   profile_begin(PA_KERNEL_COMBINE, stream);
   hipLaunchKernelGGL(decode_combine_kernel<D>, cgrid, dim3(256), 0, stream, a.seq_lens,
@@ -792,6 +857,7 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
   const int G = a.num_q_heads / a.num_kv_heads;
   if (p.qmax < 1 || p.qmax * G > 16 || (p.qmax > 1 && (p.stream || p.fused_write)))
     return hipErrorInvalidValue;
+  if (p.fused_combine && (p.stream || !p.counters)) return hipErrorInvalidValue;
   if (p.stream) {
     if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||
         decode_stream_lds_bytes(a.head_size, p.waves, a.num_seqs) > 64 * 1024)

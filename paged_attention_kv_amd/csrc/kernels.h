@@ -58,6 +58,10 @@ struct DecodePlan {
   // Partitioned schedule: rows of 1..qmax query tokens (qmax * G <= 16)
   // take the decode path; partials are laid out per query token.
   int32_t qmax;
+  // Partitioned schedule: the last workgroup of a split row merges its
+  // partials through `counters` ([S][Hkv], zero between calls) instead of a
+  // combine launch.
+  bool fused_combine;
   // Fused write (partitioned schedule, decode rows only): the decode launch
   // also writes each row's new token and reads it from knew / vnew.
   bool fused_write;
@@ -109,6 +113,7 @@ hipError_t launch_prefix(const ForwardArgs& a, const PrefixPlan& p, hipStream_t 
 struct WorkspaceLayout {
   bool stream_ok, stream_default;  // even shares fit / are the default schedule
   int32_t qmax;                    // query tokens per decode row (see DecodePlan)
+  bool fused_combine;              // partitioned rows merge in the kernel
   int32_t stream_wgs, stream_heads, stream_waves, waves, prefetch;
   int32_t part_tokens, num_parts_max, tile_queries, bound_a, bound_b;
   size_t off_ctr, off_o, off_ml, off_counts, off_tiles_a, off_tiles_b, total;

@@ -122,6 +122,17 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t waves
   return (int32_t)std::min<int64_t>(std::max<int64_t>(part, kMinPartTokens), cap);
 }
 
+// Partitioned decode with the merge in the kernel: the last workgroup of a
+// split row merges its partials, so no combine launch follows.
+// PA_DECODE_FUSED_COMBINE=0 turns it off (for comparisons). Splitting rows
+// further for balance on this path measured slower on the decode workloads
+// (the split adds workgroups and hand-overs while HBM is already the
+// limit), so partitions keep the sizes chosen above.
+bool decode_fused_combine(int32_t num_seqs, int32_t num_kv_heads) {
+  static const int v = env_int("PA_DECODE_FUSED_COMBINE", 0, 1, 1);
+  return v == 1 && (int64_t)num_seqs * num_kv_heads <= kCounterSlots;
+}
+
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 // Query tokens per row that the decode kernel takes (rows of 1..qmax
@@ -190,6 +201,7 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   w.stream_waves = kStreamWaves / w.stream_heads * w.stream_heads;
   w.stream_wgs = decode_stream_wgs();
   w.waves = decode_waves(head_size, w.prefetch);
+  w.fused_combine = decode_fused_combine(num_seqs, num_kv_heads);
   w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, w.waves, max_len);
   w.num_parts_max = (max_len + w.part_tokens - 1) / w.part_tokens;
   if (w.num_parts_max > kMaxGridZ) return false;
@@ -401,6 +413,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
   dp.counters = (int32_t*)(ws + w.off_ctr);
+  dp.fused_combine = !dp.stream && w.fused_combine;
   dp.tok_base = 0;
   dp.part_base = 0;
   dp.fused_write = fused;
@@ -614,6 +627,7 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   dp.tok_base = pl.prefix_keys;
   dp.part_base = pl.chunks;
   dp.qmax = 1;
+  dp.fused_combine = false;
   e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix decode launch");
   return PA_OK;
