@@ -138,9 +138,9 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * workgroups; small batches, or more than 4096 rows, split rows into fixed
  * partitions), rows with q_len > 1 the prefill path. When 1 <
  * max_query_len_hint <= 16 / (num_q_heads / num_kv_heads) (for instance
- * rows verifying a few speculated tokens) every row takes the partitioned
- * decode path, its q_len * G query columns sharing each K/V block, and no
- * prefill launch is made.
+ * rows verifying a few speculated tokens) every row takes the decode path
+ * (either schedule, chosen as for single-token rows), its q_len * G query
+ * columns sharing each K/V block, and no prefill launch is made.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
  * Tuning overrides, read once per process (for sweeps; out-of-range values
  * are ignored): PA_DECODE_STREAM (0 / 1 = always the partitioned / the

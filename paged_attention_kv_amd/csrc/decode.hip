@@ -1,5 +1,6 @@
-// Decode rows of the flattened batch (one query token per sequence): paged
-// attention over the sequence's whole context.
+// Decode rows of the flattened batch (one query token per sequence, or a few
+// when a step verifies drafted tokens): paged attention over the sequence's
+// whole context.
 //
 // What is computed follows the pages "Inside vLLM: Anatomy of a
 // High-Throughput LLM Inference System": section "Scheduler" (decode requests
@@ -360,7 +361,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     int32_t* __restrict__ counters, float scale_log2, int32_t Hq, int32_t Hkv, int32_t G,
-    int32_t MB, int32_t S, int32_t HG) {
+    int32_t MB, int32_t S, int32_t HG, int32_t QM) {
   using Sh = DecodeShape<D>;
   // LDS: W V slices (the merge stage overlays them), then the row prefix
   // [S + 1], scan scratch [17] and a flag.
@@ -383,20 +384,24 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
   const int grp = lane >> 4;
   const int64_t kv_row = (int64_t)Hkv * D;
 
-  // 1. Blocks per decode row (0 for other rows) and their exclusive prefix,
-  //    rows in order: thread t takes rows [t*R, t*R + R).
+  // 1. Blocks per decode row (rows of 1..QM query tokens; 0 for other rows)
+  //    and their exclusive prefix, rows in order: thread t takes rows
+  //    [t*R, t*R + R).
+  auto row_blocks = [&](int s) {
+    const int ql = qsl[s + 1] - qsl[s];
+    return (ql >= 1 && ql <= QM) ? (seq_lens[s] + kBlock - 1) / kBlock : 0;
+  };
   {
     const int R = (S + blockDim.x - 1) / blockDim.x;
     const int r_lo = min(S, (int)threadIdx.x * R);
     const int r_hi = min(S, r_lo + R);
     int mine = 0;
-    for (int s = r_lo; s < r_hi; ++s)
-      mine += (qsl[s + 1] - qsl[s] == 1) ? (seq_lens[s] + kBlock - 1) / kBlock : 0;
+    for (int s = r_lo; s < r_hi; ++s) mine += row_blocks(s);
     int total;
     int run = block_exclusive_scan(mine, tmp, &total);
     for (int s = r_lo; s < r_hi; ++s) {
       pre[s] = run;
-      run += (qsl[s + 1] - qsl[s] == 1) ? (seq_lens[s] + kBlock - 1) / kBlock : 0;
+      run += row_blocks(s);
     }
     if (threadIdx.x == 0) pre[S] = total;
     __syncthreads();
@@ -429,6 +434,8 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
     const int j_hi = (int)(min(b, r1) - a);
     pos = min(b, r1);
     const int t0 = qsl[s];
+    const int ql = qsl[s + 1] - t0;
+    const int ncols = ql * G;  // query columns: head c % G of token c / G
     const int L = seq_lens[s];
     // Shares that hold blocks of this row: p_first .. p_last.
     const int64_t p_first = ((a + 1) * P + T - 1) / T - 1;
@@ -443,7 +450,8 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
     const int nk_all = (j_hi - j_lo > sub) ? (j_hi - j_lo - 1 - sub) / Ssub + 1 : 0;
     if (head_ok && nk_all > 0) {
       bf16x8 qv[Sh::kKChunks];
-      load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, G, G, Hq);
+      load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
+      const int col_lim = L - ql + min(hl, ncols - 1) / G;  // last key of the lane's column
       const uint16_t* kbase = k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row;
       const uint16_t* vbase = v_cache + (int64_t)g * D;
       const int32_t* trow = block_table + (int64_t)s * MB + j_lo + sub;
@@ -452,22 +460,24 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
         const int ids = lane < nk ? trow[(int64_t)(kc + lane) * Ssub] : 0;
         stream_blocks<D, NBUF, kStreamV>(acc, qv, ids, nk, (j_lo + sub + kc * Ssub) * kBlock,
                                          Ssub * kBlock, L, kbase, vbase, kv_row, vl, scale_log2,
-                                         lane);
+                                         lane, NewToken{-1, nullptr, nullptr}, col_lim);
       }
       acc.lsum = sum_across_groups(acc.lsum);
     }
 
     const int my_slot = slot_of(p);
-    merge_waves<D>(acc, stage, W, HG, G, w, lane,
+    merge_waves<D>(acc, stage, W, HG, ncols, w, lane,
                    [&](int sl, int col, int d, float M, float den, float n0, float n1) {
       const int head = blockIdx.y * HG + sl;
       if (head >= Hkv) return;
-      const int qh = head * G + col;
+      const int tk = col / G;
+      const int qh = head * G + col % G;
       if (ncontrib == 1) {
         const float inv = 1.0f / den;
-        *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+        *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) =
+            pack_bf16x2(n0 * inv, n1 * inv);
       } else {  // read by the share that finishes this row last
-        const int64_t row = ((int64_t)p * 2 + my_slot) * Hq + qh;
+        const int64_t row = (((int64_t)p * 2 + my_slot) * QM + tk) * Hq + qh;
         store_coherent2(ws_o + row * D + d, n0, n1);
         if (d == 0) store_coherent2(ws_ml + row * 2, M, den);
       }
@@ -489,13 +499,16 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
       __syncthreads();
       if (*flag) {
         // Online merge in share order, eight shares' loads in flight at a
-        // time; every share's partial covers a block with a visible token,
-        // so each m is finite.
-        const int per_head = G * (D / 2);
+        // time. A share whose blocks hold no key visible to a column (the
+        // few keys past an earlier token of a several-token row) left
+        // m = -inf for it and adds nothing.
+        const int per_head = ncols * (D / 2);
         for (int idx = threadIdx.x; idx < HG * per_head; idx += blockDim.x) {
           const int head = blockIdx.y * HG + idx / per_head;
           if (head >= Hkv) continue;
-          const int qh = head * G + (idx % per_head) / (D / 2);
+          const int col = (idx % per_head) / (D / 2);
+          const int tk = col / G;
+          const int qh = head * G + col % G;
           const int d = 2 * (idx % (D / 2));
           float M = -INFINITY, den = 0.f, n0 = 0.f, n1 = 0.f;
           for (int64_t c0 = p_first; c0 <= p_last; c0 += 8) {
@@ -503,15 +516,15 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
               const int64_t c = min(c0 + k, p_last);
-              const int64_t row = (c * 2 + slot_of(c)) * Hq + qh;
+              const int64_t row = ((c * 2 + slot_of(c)) * QM + tk) * Hq + qh;
               ml[k] = load_coherent2(ws_ml + row * 2);
               ov[k] = load_coherent2(ws_o + row * D + d);
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-              if (c0 + k <= p_last) {
+              if (c0 + k <= p_last && ml[k][0] != -INFINITY) {
                 const float mn = fmaxf(M, ml[k][0]);
-                const float sc = fast_exp2(M - mn);
+                const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mn);
                 const float e = fast_exp2(ml[k][0] - mn);
                 den = den * sc + e * ml[k][1];
                 n0 = n0 * sc + e * ov[k][0];
@@ -521,7 +534,8 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
             }
           }
           const float inv = 1.0f / den;
-          *(uint32_t*)(out + ((int64_t)t0 * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
+          *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) =
+              pack_bf16x2(n0 * inv, n1 * inv);
         }
       }
     }
@@ -791,7 +805,7 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens,
                        a.query_start_loc, (uint16_t*)a.out, p.ws_o, p.ws_ml, p.counters,
                        scale_log2, a.num_q_heads, a.num_kv_heads, G, a.max_blocks_per_seq,
-                       a.num_seqs, p.stream_heads);
+                       a.num_seqs, p.stream_heads, p.qmax);
     profile_end(PA_KERNEL_DECODE, stream);
     return hipGetLastError();
   }
@@ -855,7 +869,7 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
       p.num_parts_max - p.part_base < 1 || ((p.tok_base || p.part_base) && p.stream))
     return hipErrorInvalidValue;
   const int G = a.num_q_heads / a.num_kv_heads;
-  if (p.qmax < 1 || p.qmax * G > 16 || (p.qmax > 1 && (p.stream || p.fused_write)))
+  if (p.qmax < 1 || p.qmax * G > 16 || (p.qmax > 1 && p.fused_write))
     return hipErrorInvalidValue;
   if (p.fused_combine && (p.stream || !p.counters)) return hipErrorInvalidValue;
   if (p.stream) {

@@ -205,10 +205,11 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, w.waves, max_len);
   w.num_parts_max = (max_len + w.part_tokens - 1) / w.part_tokens;
   if (w.num_parts_max > kMaxGridZ) return false;
-  const size_t stream_rows = w.stream_ok ? (size_t)w.stream_wgs * 2 * num_q_heads : 0;
+  const size_t stream_rows = w.stream_ok ? (size_t)w.stream_wgs * 2 * w.qmax * num_q_heads : 0;
   const size_t part_rows =
       w.num_parts_max > 1 ? (size_t)num_seqs * w.num_parts_max * w.qmax * num_q_heads : 0;
-  const size_t rows = std::max(stream_rows, part_rows);  // (share, slot, head) / (row, part, head)
+  // (share, slot, token, head) / (row, part, token, head)
+  const size_t rows = std::max(stream_rows, part_rows);
   const size_t dec_o = rows * head_size, dec_ml = rows * 2;
   w.tile_queries = prefill_tile_queries(group);
   const int32_t bq_b = prefill_split_tile_queries(group);
@@ -376,9 +377,9 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   char* ws = (char*)workspace;
 
   pa::DecodePlan dp;
-  dp.stream = w.qmax == 1 && ((flags & PA_FORWARD_DECODE_EVEN_SHARES)    ? w.stream_ok
-                              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
-                                                                        : w.stream_default);
+  dp.stream = (flags & PA_FORWARD_DECODE_EVEN_SHARES)   ? w.stream_ok
+              : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
+                                                        : w.stream_default;
   dp.qmax = w.qmax;
   const bool fused = wr && max_query_len_hint == 1 && !dp.stream;
   if (wr && !fused) {

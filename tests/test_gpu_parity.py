@@ -208,22 +208,53 @@ def test_multi_token_decode_rows(name, hq, hkv, d, rows, hinted):
     assert_close(out.cpu()[r], want, name)
 
 
-def test_multi_token_decode_rows_nan_poison_and_schedules():
+@pytest.mark.parametrize("schedule", ["even", "partitioned"])
+@pytest.mark.parametrize("name,hq,hkv,d,rows", MULTI_TOKEN_CASES,
+                         ids=[c[0] for c in MULTI_TOKEN_CASES])
+def test_multi_token_decode_rows_schedules(name, hq, hkv, d, rows, schedule):
+    """The same rows on each decode schedule by flag. Even shares cut rows
+    anywhere, so a share can hold only the last few keys of a row, none of
+    them visible to its earlier tokens."""
+    spec = wl.custom(name, hq, hkv, d, rows=rows, seed=140 + len(rows))
+    banner(f"multi-token decode rows {name}: schedule {schedule} q_lens={spec.q_lens}")
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case, hints=True, decode_schedule=schedule)
+    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
+    r, want = oracle_rows(case, seqs)
+    assert_close(out.cpu()[r], want, f"{name} {schedule}")
+
+
+def test_multi_token_decode_rows_on_many_shares():
+    """Rows of 4 tokens whose last block holds 1..3 keys, so many even
+    shares end inside the causal tail; 512 shares over few blocks."""
+    # (q_len, prior context): seq_len % 16 is 1, 2 or 3 for the first six
+    rows = [(4, 16 * k + j) for k, j in [(3, 13), (0, 14), (7, 15), (1, 13), (12, 14), (2, 15)]]
+    rows += [(3, 14), (2, 15), (1, 31)]
+    spec = wl.custom("mt_shares", 32, 8, 64, rows=rows, seed=151)
+    case = wl.make_case(spec, device=DEV)
+    out = write_and_forward(case, hints=True, decode_schedule="even")
+    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[r], want, "many shares")
+
+
+@pytest.mark.parametrize("schedule", ["partitioned", "even"])
+def test_multi_token_decode_rows_nan_poison_and_schedules(schedule):
     """NaN in every cache row outside the contexts; rows of 4 tokens split
-    into many partitions, against the oracle."""
+    into many partitions or shares, against the oracle."""
     rows = [(4, 9000), (4, 100), (4, 3), (2, 4000)]
     spec = wl.custom("mt_nan", 32, 8, 128, rows=rows, seed=150)
     case = wl.make_case(spec, device=DEV, poison=float("nan"))
-    out = write_and_forward(case, hints=True, decode_schedule="partitioned")
+    out = write_and_forward(case, hints=True, decode_schedule=schedule)
     r, want = oracle_rows(case, list(range(spec.num_seqs)))
-    assert_close(out.cpu()[r], want, "nan poison")
+    assert_close(out.cpu()[r], want, f"nan poison {schedule}")
 
 
-def test_spec_decode_workload_sampled_rows():
+@pytest.mark.parametrize("schedule", [None, "even", "partitioned"])
+def test_spec_decode_workload_sampled_rows(schedule):
     spec = wl.spec_decode(4)
-    banner("speculative-verify workload: 256 rows x 4 query tokens")
+    banner(f"speculative-verify workload: 256 rows x 4 query tokens, schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case).cpu()
+    out = write_and_forward(case, decode_schedule=schedule).cpu()
     pick = sorted(random.Random(16).sample(range(256), 10) + [0, 255])
     r, want = oracle_rows(case, pick)
     assert_close(out[r], want, "spec decode")
