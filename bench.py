@@ -216,6 +216,40 @@ def run_graph_steps(pa, inp: StepInputs, steps: int, warmup: int) -> float:
     return t0.elapsed_time(t1) / steps
 
 
+PROBE_SHAPES = ((4, 16), (8, 16), (16, 16), (8, 8), (4, 32), (8, 32), (16, 32), (8, 64))
+
+
+def run_read_probe(pa, inp: StepInputs, steps: int, warmup: int):
+    """The library's read probe (every K and V block of the step's rows read
+    whole, no arithmetic) over the same block-table rotations, for a few
+    launch shapes (waves, table columns per workgroup); returns (best ms per
+    launch, its shape, bytes per launch)."""
+    spec = inp.spec
+    blk = wl.BLOCK_SIZE * spec.num_kv_heads * spec.head_size * 2 * 2
+    nbytes = sum(-(-L // wl.BLOCK_SIZE) for L in spec.seq_lens) * blk
+    sink = torch.zeros(1, dtype=torch.int32, device=inp.k_cache.device)
+    best = None
+    for shape in PROBE_SHAPES:
+        def launch(i):
+            st = inp.sets[i % inp.rotations]
+            pa.probe_block_read(inp.k_cache, inp.v_cache, st["block_table"], inp.seq_lens,
+                                waves=shape[0], blocks_per_workgroup=shape[1], sink=sink)
+        for i in range(warmup):
+            launch(i)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            launch(i)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        if best is None or ms < best[0]:
+            best = (ms, shape)
+    return best[0], best[1], nbytes
+
+
 def sub_spec(spec, rows, name):
     """The same rows as a workload of their own (for attributing time)."""
     return wl.Spec(name, spec.num_q_heads, spec.num_kv_heads, spec.head_size,
@@ -331,13 +365,20 @@ def main(argv=None):
         b_step = b_attn + write_bytes(spec)
         gbs = b_step / (ms_step * 1e-3) / 1e9
         ms_graph = run_graph_steps(pa, inp, args.steps, args.warmup)
-        ms_dec = kmean["decode"]
+        ms_probe, probe_shape, probe_bytes = run_read_probe(pa, inp, args.steps, args.warmup)
         fused = "cache_write" not in kcount  # the decode launch also wrote the new tokens
+        one_launch = set(kcount) == {"decode"} and abs(kcount["decode"] - 1.0) < 1e-9
+        # A step that is one launch: its duration is the events around the
+        # whole timed region over the launches in it (gaps between launches
+        # included, so never shorter than the kernel). Events around each
+        # launch add their own packets to it and read longer.
+        ms_dec = ms_step if one_launch else kmean["decode"]
         b_dec = b_step if fused else b_attn
         result["decode"] = dict(ms_step=ms_step, gbs=gbs, ms_fwd=ms_fwd, ms_decode_kernel=ms_dec,
                                 kernel_gbs=b_dec / (ms_dec * 1e-3) / 1e9, bytes_step=b_step,
                                 bytes_fwd=b_dec, fused=fused, rotations=inp.rotations,
-                                ms_graph=ms_graph,
+                                ms_graph=ms_graph, one_launch=one_launch,
+                                probe=(ms_probe, probe_shape, probe_bytes),
                                 kernels={k: round(v * 1e3, 3) for k, v in kmean.items()})
         del inp
         torch.cuda.empty_cache()
@@ -437,9 +478,21 @@ def main(argv=None):
                             "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic(kname, "decode ("),
                             "avg_launch_us": round(d["ms_decode_kernel"] * 1e3, 3),
+                            "avg_launch_us_from": ("events around the timed region / launches"
+                                                   if d["one_launch"] else
+                                                   "events around each launch"),
                             "algorithmic_bytes_per_launch": d["bytes_fwd"],
                             "forward_kernels_us_per_step": round(d["ms_fwd"] * 1e3, 3),
                             "kernel_avg_us": d["kernels"]}
+        pms, pshape, pbytes = d["probe"]
+        pgbs = pbytes / (pms * 1e-3) / 1e9
+        line["roofline"]["read_probe"] = {
+            "what": "the same blocks read whole with no arithmetic (pa_probe_block_read), "
+                    "best of %d launch shapes" % len(PROBE_SHAPES),
+            "us": round(pms * 1e3, 3), "bytes": pbytes, "gbs": round(pgbs, 1),
+            "frac_of_peak": round(pgbs / HBM_PEAK_GBS, 4),
+            "waves_blocks_per_wg": list(pshape),
+            "kernel_frac_of_probe": round(d["kernel_gbs"] / pgbs, 4)}
     if "mixed" in result:
         m = result["mixed"]
         pre = m["sub"]["prefill_rows"]

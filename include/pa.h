@@ -284,6 +284,36 @@ int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
                        int32_t max_query_len_hint, int32_t max_seq_len_hint, void* stream);
 
 /*
+ * Read probe for measurement harnesses (not part of the attention path):
+ * reads every K and V block that rows 0..num_seqs-1 cover (the first
+ * ceil(seq_lens[s] / 16) entries of each table row, the blocks a forward
+ * call reads for them; section "Run forward pass"), whole and once, with
+ * no arithmetic, so a decode kernel's bandwidth can be set beside what the
+ * memory system delivers for the same scattered blocks. Bytes read:
+ * sum over rows of ceil(seq_len / 16) * 2 * 16 * num_kv_heads * head_size
+ * * 2.
+ *
+ *   k_cache, v_cache   device, bf16 [num_blocks, 16, num_kv_heads, head_size],
+ *                      16-byte aligned; only read
+ *   block_table        device, int32 [num_seqs, max_blocks_per_seq]; ids
+ *                      outside [0, num_blocks) are clamped into it
+ *   seq_lens           device, int32 [num_seqs], each <= max_blocks_per_seq * 16
+ *   waves              waves per workgroup, 1..16
+ *   blocks_per_workgroup  table columns per workgroup, >= 1; the grid is
+ *                      num_seqs x ceil(max_blocks_per_seq / blocks_per_workgroup)
+ *   sink               device, 4 bytes; written only if the XOR of all data
+ *                      read by one thread equals 0x9e3779b9 (keeps the
+ *                      loads from being optimised away)
+ *
+ * Enqueues one launch on `stream` and returns; PA_ERR_* on a bad argument.
+ */
+int pa_probe_block_read(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                        int32_t head_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                        int32_t waves, int32_t blocks_per_workgroup, uint32_t* sink,
+                        void* stream);
+
+/*
  * Kernel timing for measurement harnesses (not for the hot path). After
  * pa_profile_begin, every kernel the library launches is bracketed by HIP
  * events on its stream; pa_profile_end stops recording, waits for those

@@ -80,6 +80,8 @@ SIGNATURES = {
                                             _I32, _I32, _P, _SZ, ctypes.c_uint32, _P]),
     "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                           _I32, _I32, _P]),
+    "pa_probe_block_read": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
+                                           _I32, _P, _P]),
     "pa_profile_begin": (ctypes.c_int, []),
     "pa_profile_end": (ctypes.c_int, [_P]),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -364,6 +366,30 @@ def validate_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor,
                                   num_tokens, S, MB, num_blocks, BLOCK_SIZE, nw,
                                   max_query_len or 0, max_seq_len or 0,
                                   _stream(block_table)))
+
+
+def probe_block_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, waves: int = 8, blocks_per_workgroup: int = 16,
+                     sink: Optional[torch.Tensor] = None) -> None:
+    """Read every K and V block the rows cover, whole, with no arithmetic (a
+    measurement probe for the memory system on the decode read pattern; see
+    pa_probe_block_read). Enqueued on the current stream."""
+    lib = load_library()
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(n, t, torch.bfloat16, 4)
+    _dev_tensor("block_table", block_table, torch.int32, 2)
+    _dev_tensor("seq_lens", seq_lens, torch.int32, 1)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache differ in shape")
+    S, MB = block_table.shape
+    if seq_lens.shape[0] != S:
+        raise ValueError("seq_lens must have one entry per table row")
+    NB, _, Hkv, D = k_cache.shape
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=k_cache.device)
+    _check(lib.pa_probe_block_read(k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                   seq_lens.data_ptr(), S, Hkv, D, MB, NB, waves,
+                                   blocks_per_workgroup, sink.data_ptr(), _stream(k_cache)))
 
 
 def profile_begin() -> None:

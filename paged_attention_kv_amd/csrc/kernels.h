@@ -15,6 +15,12 @@ namespace pa {
 void profile_begin(int cls, hipStream_t stream);
 void profile_end(int cls, hipStream_t stream);
 
+// Read probe: the rows' K and V blocks read whole, no arithmetic.
+hipError_t launch_block_read_probe(const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_kv_heads, int32_t head_size,
+                                   int32_t max_blocks_per_seq, int64_t num_blocks, int32_t waves,
+                                   int32_t blocks_per_wg, uint32_t* sink, hipStream_t stream);
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
                               void* k_cache, void* v_cache, int32_t num_tokens,
                               int32_t num_kv_heads, int32_t head_size, hipStream_t stream);

@@ -634,6 +634,31 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   return PA_OK;
 }
 
+int pa_probe_block_read(const void* k_cache, const void* v_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                        int32_t head_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                        int32_t waves, int32_t blocks_per_workgroup, uint32_t* sink,
+                        void* stream) {
+  g_last_error.clear();
+  if (num_seqs <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || waves < 1 || waves > 16 || blocks_per_workgroup < 1 ||
+      (max_blocks_per_seq + (int64_t)blocks_per_workgroup - 1) / blocks_per_workgroup > 65535)
+    return fail(PA_ERR_SHAPE, "pa_probe_block_read: a size is out of range");
+  if ((head_size * num_kv_heads) % 8 || (int64_t)16 * num_kv_heads * head_size / 8 > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "pa_probe_block_read: unsupported block shape");
+  if (!k_cache || !v_cache || !block_table || !seq_lens || !sink)
+    return fail(PA_ERR_NULL, "pa_probe_block_read: null pointer argument");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(sink, 4))
+    return fail(PA_ERR_ALIGN, "pa_probe_block_read: caches must be 16-byte aligned");
+  hipError_t e = pa::launch_block_read_probe(k_cache, v_cache, block_table, seq_lens, num_seqs,
+                                             num_kv_heads, head_size, max_blocks_per_seq,
+                                             num_blocks, waves, blocks_per_workgroup, sink,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pa_probe_block_read launch");
+  return PA_OK;
+}
+
 int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
                        const int32_t* query_start_loc, const int64_t* slot_mapping,
                        int32_t num_tokens, int32_t num_seqs, int32_t max_blocks_per_seq,

@@ -113,6 +113,23 @@ def test_validate_rejects_null_before_touching_the_device(lib):
     assert lib.pa_validate_inputs(FAKE, FAKE, FAKE, None, 4, 2, 4, 64, 8, 0, 0, 0, None) == -3
 
 
+def test_read_probe_rejects_bad_arguments(lib):
+    def probe(**kw):
+        a = dict(kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, S=2, Hkv=4, D=64, MB=4, NB=64, W=8, C=16,
+                 sink=FAKE)
+        a.update(kw)
+        return lib.pa_probe_block_read(a["kc"], a["vc"], a["bt"], a["sl"], a["S"], a["Hkv"],
+                                       a["D"], a["MB"], a["NB"], a["W"], a["C"], a["sink"], None)
+    assert probe(kc=NULL) == -1
+    assert probe(sink=NULL) == -1
+    assert probe(S=0) == -2
+    assert probe(W=0) == -2 and probe(W=17) == -2
+    assert probe(C=0) == -2
+    assert probe(MB=1 << 20, C=1) == -2   # grid y past 65535
+    assert probe(D=3, Hkv=1) == -3
+    assert probe(vc=FAKE + 8) == -4
+
+
 @pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
 def test_workspace_sizes_for_the_named_workloads(lib, i):
     s = wl.config(i)

@@ -639,3 +639,22 @@ def test_kernel_timing_records_each_launch_class():
     # timing does not change results
     r, want = oracle_rows(case, list(range(spec.num_seqs)))
     assert_close(out.cpu()[r], want, "profiled forward")
+
+
+# ---------------------------------------------------------------------------
+# Read probe (measurement only)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("waves,per_wg", [(4, 16), (16, 8), (1, 1)])
+def test_read_probe_only_reads(waves, per_wg):
+    spec = wl.config(2)
+    banner(f"read probe on workload 2: waves {waves}, {per_wg} blocks per workgroup")
+    case = wl.make_case(spec, device=DEV)
+    kc0 = case.k_cache[:4096].clone()
+    vc0 = case.v_cache[-4096:].clone()
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pa.probe_block_read(case.k_cache, case.v_cache, case.block_table, case.seq_lens, waves=waves,
+                        blocks_per_workgroup=per_wg, sink=sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) in (0, 0x9E3779B9 - (1 << 32))
+    assert torch.equal(case.k_cache[:4096], kc0) and torch.equal(case.v_cache[-4096:], vc0)
