@@ -51,6 +51,9 @@ namespace pa {
 namespace {
 
 constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
+// Fourth word of a raw buffer resource on gfx9-family chips: 32-bit data
+// format, so buffer loads move raw bytes.
+constexpr int kBufferWordFlags = 0x00020000;
 
 template <int D>
 struct DecodeShape {
@@ -70,9 +73,11 @@ struct DecodeShape {
 };
 
 // Most waves per decode workgroup: as many as fit on a CU at the kernel's
-// register use (<= 128 VGPRs: 4 waves per SIMD; <= 168: 3).
-template <int D, int NBUF>
-constexpr int max_waves() { return (D == 64 && NBUF == 2) ? 16 : 12; }
+// register use (<= 128 VGPRs: 4 waves per SIMD; <= 168: 3). The fused-write
+// variants beyond D = 64 with two blocks in flight need more registers than
+// 168 and take at most 8 waves (<= 256 VGPRs), so they do not spill.
+template <int D, int NBUF, bool kWrite = false>
+constexpr int max_waves() { return (D == 64 && NBUF == 2) ? 16 : (kWrite ? 8 : 12); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -119,23 +124,37 @@ struct WaveAcc {
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qv)[D / 32], const uint16_t* __restrict__ qrow,
                                        int hl, int grp, int ncols, int G, int Hq) {
+  // (every lane loads, from a valid column, so no branch guards the loads)
   const int col = hl < ncols ? hl : 0;
   const u32x4* qp = (const u32x4*)(qrow + ((int64_t)(col / G) * Hq + col % G) * D) + grp;
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    qv[i] = as_bf16x8(hl < ncols ? qp[4 * i] : z);
+    const u32x4 t = qp[4 * i];
+    qv[i] = as_bf16x8(hl < ncols ? t : z);
   }
 }
 
 // Where a kernel also writes the step's new tokens into the cache (the fused
 // write), it reads the row's newest token from the step's own k and v, not
-// from the cache slot being written in the same launch.
+// from the cache slot being written in the same launch, unless the slot is
+// negative (nothing is written and the cache holds the token, as after a
+// separate write). The slot sits in lane 0 of `slot`, loaded by a vector
+// load at the start and first read when the wave loads its last block, so
+// the blocks start streaming before it arrives.
 struct NewToken {
   int tok;                          // its position in the row (-1: none)
   const uint16_t* __restrict__ k;   // its K of this KV head (D elements)
   const uint16_t* __restrict__ v;   // its V of this KV head
+  int64_t slot;                     // lane 0: its slot_mapping entry
 };
+
+// Lane 0's value of a 64-bit register, as a wave-uniform value.
+__device__ __forceinline__ int64_t first_lane64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Streams nk (1..64) blocks of one KV head into acc: block k's id sits in lane
 // k of `ids`, its first token is tok0 + k * tok_step, and tokens >= tok_end
@@ -151,7 +170,7 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
                                               const uint16_t* __restrict__ kbase,
                                               const uint16_t* __restrict__ vbase, int64_t kv_row,
                                               uint16_t* vl, float scale_log2, int lane,
-                                              NewToken nt = NewToken{-1, nullptr, nullptr},
+                                              NewToken nt = NewToken{-1, nullptr, nullptr, -1},
                                               int col_lim = INT32_MAX) {
   using Sh = DecodeShape<D>;
   const int hl = lane & 15;
@@ -167,21 +186,33 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
     const int64_t blk = __builtin_amdgcn_readlane(ids, kc);
     const int64_t boff = blk * kBlock * kv_row;
     const u32x4* kp = (const u32x4*)(kbase + boff);
-    if constexpr (kNew) {
-      if (tok0 + kc * tok_step + hl == nt.tok) kp = (const u32x4*)(nt.k + 8 * grp);
-    }
 #pragma unroll
     for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = kp[4 * i];
 #pragma unroll
     for (int c = 0; c < Sh::kVChunks; ++c) {
       const int idx = c * kWave + lane;
-      const int row = idx / (D / 8);
-      const int col8 = idx % (D / 8);
-      const u32x4* vp = (const u32x4*)(vbase + boff + row * kv_row + col8 * 8);
-      if constexpr (kNew) {
-        if (tok0 + kc * tok_step + row == nt.tok) vp = (const u32x4*)(nt.v + col8 * 8);
-      }
+      const u32x4* vp = (const u32x4*)(vbase + boff + (idx / (D / 8)) * kv_row + (idx % (D / 8)) * 8);
       vv[c] = kStreamV ? __builtin_nontemporal_load(vp) : *vp;
+    }
+    if constexpr (kNew) {
+      // One block of the row holds its newest token: the wave that streams
+      // it reads the slot here, long after its load returned, and then
+      // replaces that token's row with the step's own K and V. Both tests
+      // are wave-uniform branches, so every other block pays two scalar
+      // instructions after its loads.
+      const int tokb = tok0 + kc * tok_step;
+      if (tokb == (nt.tok & ~(kBlock - 1)) && first_lane64(nt.slot) >= 0) {
+        const int r = nt.tok - tokb;  // the token's row in the block
+        if (hl == r) {
+#pragma unroll
+          for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = ((const u32x4*)(nt.k + 8 * grp))[4 * i];
+        }
+#pragma unroll
+        for (int c = 0; c < Sh::kVChunks; ++c) {
+          const int idx = c * kWave + lane;
+          if (idx / (D / 8) == r) vv[c] = *(const u32x4*)(nt.v + (idx % (D / 8)) * 8);
+        }
+      }
     }
   };
 
@@ -460,7 +491,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
         const int ids = lane < nk ? trow[(int64_t)(kc + lane) * Ssub] : 0;
         stream_blocks<D, NBUF, kStreamV>(acc, qv, ids, nk, (j_lo + sub + kc * Ssub) * kBlock,
                                          Ssub * kBlock, L, kbase, vbase, kv_row, vl, scale_log2,
-                                         lane, NewToken{-1, nullptr, nullptr}, col_lim);
+                                         lane, NewToken{-1, nullptr, nullptr, -1}, col_lim);
       }
       acc.lsum = sum_across_groups(acc.lsum);
     }
@@ -552,7 +583,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
 // partition writes its KV head's slice, and every workgroup reads that token
 // from knew / vnew.
 template <int D, int NBUF, bool kStreamV, bool kWrite>
-__global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
+__global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
@@ -589,13 +620,16 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   // Rows of 1..QM query tokens: token i of the row sits at position
   // L - ql + i and sees keys up to it; the row's ql * G (<= 16) query
   // columns share every K/V block.
+  // (the row's start, query count and length are loaded together, ahead of
+  // any use, so they cost one round trip)
   const int t0 = qsl[s];
-  const int ql = qsl[s + 1] - t0;
-  if (ql < 1 || ql > QM) return;  // not a decode row
-  const int ncols = ql * G;
+  const int t1 = qsl[s + 1];
   const int L = seq_lens[s];
+  __builtin_amdgcn_sched_barrier(0);
+  const int ql = t1 - t0;
   const int tok_begin = tok_base + part * part_tokens;
-  if (tok_begin >= L) return;
+  if (ql < 1 || ql > QM || tok_begin >= L) return;  // not a decode row / past its end
+  const int ncols = ql * G;
   const int tok_end = min(L, tok_begin + part_tokens);
   const int nparts = (L - tok_base + part_tokens - 1) / part_tokens;
   const int nblk = (tok_end + kBlock - 1) / kBlock - b_begin;
@@ -603,34 +637,52 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_kernel(
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int64_t kv_row = (int64_t)Hkv * D;
-  NewToken nt{-1, nullptr, nullptr};
+  NewToken nt{-1, nullptr, nullptr, -1};
+  // The fused write: wave 0 of the row's last partition stores its KV head's
+  // slice of the new token after streaming (lanes < 2 * D / 8, 16 bytes
+  // each: K, then V). The slot is loaded here by every wave with a vector
+  // load (a buffer load, which is never turned into a scalar one), so that
+  // nothing waits for it before the blocks start streaming. A negative slot
+  // writes nothing. At D = 64 the token's data and q are also loaded here,
+  // unconditionally, so the wait for the block ids does not include them;
+  // at D = 128 the registers to hold them that long are not there.
+  constexpr bool kEarly = D == 64;
+  auto new_token_data = [&]() {
+    return *(const u32x4*)(((lane % (2 * (D / 8))) >= D / 8 ? nt.v : nt.k) + (lane % (D / 8)) * 8);
+  };
+  u32x4 wval = {0u, 0u, 0u, 0u};
   if constexpr (kWrite) {
-    // A negative slot writes nothing, and the token is then read from the
-    // cache like every other, as a separate write launch would leave it.
-    const int64_t slot = slot_mapping[t0];
-    if (slot >= 0) {
-      nt = NewToken{L - 1, knew + ((int64_t)t0 * Hkv + g) * D, vnew + ((int64_t)t0 * Hkv + g) * D};
-      if (part == nparts - 1 && w == 0 && lane < 2 * (D / 8)) {
-        // [NB, 16, Hkv, D]: the slot's row starts at element slot * Hkv * D
-        const int c8 = lane % (D / 8);
-        const bool isv = lane >= D / 8;
-        const u32x4 val = *(const u32x4*)((isv ? nt.v : nt.k) + c8 * 8);
-        *(u32x4*)((isv ? v_cache_w : k_cache_w) + slot * kv_row + (int64_t)g * D + c8 * 8) = val;
-      }
-    }
+    nt = NewToken{L - 1, knew + ((int64_t)t0 * Hkv + g) * D, vnew + ((int64_t)t0 * Hkv + g) * D,
+                  -1};
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(slot_mapping + t0), (short)0, (int)sizeof(int64_t), kBufferWordFlags);
+    nt.slot = __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(srs, 0, 0, 0));
+    if constexpr (kEarly) wval = new_token_data();
   }
+  bf16x8 qv[Sh::kKChunks];
+  if constexpr (kEarly) load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
 
   WaveAcc<D> acc;
   acc.init();
   if (nmine > 0) {
-    bf16x8 qv[Sh::kKChunks];
-    load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
+    if constexpr (!kEarly)
+      load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
     const int col_lim = L - ql + min(hl, ncols - 1) / G;  // last key of the lane's column
     stream_blocks<D, NBUF, kStreamV, kWrite>(
         acc, qv, my_blk, nmine, (b_begin + w) * kBlock, W * kBlock, tok_end,
         k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row, v_cache + (int64_t)g * D,
         kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt, col_lim);
     acc.lsum = sum_across_groups(acc.lsum);
+  }
+  if constexpr (kWrite) {
+    if (part == nparts - 1 && w == 0) {  // wave-uniform
+      // [NB, 16, Hkv, D]: the slot's row starts at element slot * Hkv * D
+      const int64_t slot = first_lane64(nt.slot);
+      if constexpr (!kEarly) wval = new_token_data();
+      if (slot >= 0 && lane < 2 * (D / 8))
+        *(u32x4*)((lane >= D / 8 ? v_cache_w : k_cache_w) + slot * kv_row + (int64_t)g * D +
+                  (lane % (D / 8)) * 8) = wval;
+    }
   }
 
   // With counters, the workgroup that finishes a split row last merges its
@@ -846,10 +898,12 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
 
 }  // namespace
 
-int32_t decode_max_waves(int32_t head_size, int32_t prefetch) {
+int32_t decode_max_waves(int32_t head_size, int32_t prefetch, bool fused_write) {
   switch (head_size) {
-    case 64: return prefetch >= 3 ? max_waves<64, 3>() : max_waves<64, 2>();
-    case 128: return max_waves<128, 2>();
+    case 64:
+      if (prefetch >= 3) return fused_write ? max_waves<64, 3, true>() : max_waves<64, 3>();
+      return fused_write ? max_waves<64, 2, true>() : max_waves<64, 2>();
+    case 128: return fused_write ? max_waves<128, 2, true>() : max_waves<128, 2>();
     default: return 0;
   }
 }
@@ -860,7 +914,7 @@ size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seq
 }
 
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
-  const int maxw = decode_max_waves(a.head_size, p.prefetch);
+  const int maxw = decode_max_waves(a.head_size, p.prefetch, p.fused_write);
   if (p.waves < 1 || p.waves > maxw || a.num_kv_heads > 65535) return hipErrorInvalidValue;
   if (p.fused_write && (p.stream || !p.knew || !p.vnew || !p.slot_mapping || !p.k_cache_w ||
                         !p.v_cache_w))

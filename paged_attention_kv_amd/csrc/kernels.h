@@ -78,9 +78,9 @@ struct DecodePlan {
   void* v_cache_w;
 };
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream);
-// Most waves a decode workgroup may hold for this head size and ring depth
-// (0: head size not built).
-int32_t decode_max_waves(int32_t head_size, int32_t prefetch);
+// Most waves a decode workgroup may hold for this head size and ring depth,
+// of the fused-write variant or the others (0: head size not built).
+int32_t decode_max_waves(int32_t head_size, int32_t prefetch, bool fused_write = false);
 // LDS bytes of one stream-schedule workgroup.
 size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seqs);
 

@@ -302,9 +302,9 @@ struct WriteArgs {
 };
 
 // pa_forward_ex, optionally preceded by the step's KV write (wr): fused into
-// the decode launch when every row is a decode row (max_query_len_hint == 1)
-// and the rows take the partitioned schedule, else a cache-write launch
-// first.
+// the decode launch when every row is a decode row (max_query_len_hint == 1),
+// the rows take the partitioned schedule and its waves fit the fused
+// kernel's bound, else a cache-write launch first.
 int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_table, const int32_t* seq_lens,
                  const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
@@ -381,7 +381,8 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
               : (flags & PA_FORWARD_DECODE_PARTITIONED) ? false
                                                         : w.stream_default;
   dp.qmax = w.qmax;
-  const bool fused = wr && max_query_len_hint == 1 && !dp.stream;
+  const bool fused = wr && max_query_len_hint == 1 && !dp.stream &&
+                     w.waves <= pa::decode_max_waves(head_size, w.prefetch, true);
   if (wr && !fused) {
     hipError_t e = pa::launch_cache_write(wr->k, wr->v, wr->slot_mapping, wr->k_cache,
                                           wr->v_cache, num_tokens, num_kv_heads, head_size, st);
