@@ -99,6 +99,8 @@ hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_
 // tiles whose rows see many keys (list A) and few (list B).
 int32_t prefill_tile_queries(int32_t group);
 int32_t prefill_split_tile_queries(int32_t group);
+// Decode rows per workgroup of the shared-prefix pass.
+int32_t prefix_tile_rows(int32_t group);
 // Upper bound on list-B tiles per row.
 int32_t prefill_split_tiles_per_row(int32_t group);
 

@@ -498,7 +498,7 @@ bool plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, in
   PrefixLayout p;
   p.prefix_keys = prefix_blocks * PA_BLOCK_SIZE;
   if (max_len <= p.prefix_keys) return false;
-  const int32_t rows = pa::prefill_tile_queries(group);
+  const int32_t rows = pa::prefix_tile_rows(group);
   const int64_t row_tiles = (num_seqs + rows - 1) / rows;
   const int64_t want = std::max<int64_t>(1, (kComputeUnits + row_tiles * num_kv_heads - 1) /
                                                 (row_tiles * num_kv_heads));

@@ -44,6 +44,11 @@ namespace {
 // hi + lo, which needs more registers): 4 waves (128 rows), two stages.
 constexpr int kWavesA = 8, kStagesA = 2;
 constexpr int kWavesB = 4, kStagesB = 2;
+constexpr int kWavesP = 8;  // shared-prefix pass
+// 16-row MFMA tiles per wave (32 rows; 64 rows per wave, which would halve
+// the LDS reads per MFMA, needs more than the 512 registers of one wave per
+// SIMD in this form): list A, the others.
+constexpr int kRowTilesA = 2, kRowTiles = 2;
 constexpr int kKeysPerTile = 64;
 constexpr float kLazyP = 8.0f;  // log2 of the largest unnormalised weight
 constexpr int kSplitKeys = 128;  // workgroups seeing at most this many keys split P
@@ -173,7 +178,8 @@ struct PrefixArgs {
 };
 
 template <int D, int G, int MODE>
-__global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) void prefill_tile_kernel(
+__global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWavesP : kWavesA) * kWave,
+                             1) void prefill_tile_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
@@ -182,9 +188,11 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     int32_t MB, int32_t tile_bound, PrefixArgs pfx) {
   constexpr bool SPLIT = MODE == kListB;
   constexpr bool PREFIX = MODE == kPrefix;
-  constexpr int NW = SPLIT ? kWavesB : kWavesA;   // waves
+  constexpr int NW = SPLIT ? kWavesB : PREFIX ? kWavesP : kWavesA;  // waves
   constexpr int NST = SPLIT ? kStagesB : kStagesA;  // LDS stages
-  constexpr int BQ = 32 * NW / G;             // query tokens per tile
+  constexpr int MT = MODE == kListA ? kRowTilesA : kRowTiles;  // 16-row tiles per wave
+  constexpr int RW = 16 * MT;                 // rows per wave
+  constexpr int BQ = RW * NW / G;             // query tokens per tile
   constexpr int BN = kKeysPerTile;            // keys per iteration
   constexpr int RB = D * 2;                   // bytes of one K or V row (unpadded)
   constexpr int KC = D / 32;                  // QK MFMAs per 16x16 S tile
@@ -243,12 +251,12 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
   const int grp = lane >> 4;
   const int64_t kv_row = (int64_t)Hkv * D;
 
-  // Rows of this lane (one per m-tile): row = w*32 + mt*16 + hl = token*G + head.
-  bf16x8 qv[2][KC];
-  int lim[2];
+  // Rows of this lane (one per m-tile): row = w*RW + mt*16 + hl = token*G + head.
+  bf16x8 qv[MT][KC];
+  int lim[MT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int row = w * 32 + mt * 16 + hl;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = w * RW + mt * 16 + hl;
     const int tl = row / G;
     const int hh = row % G;
     const bool ok = tl < nq;
@@ -268,16 +276,19 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     }
   }
 
-  f32x4 o[2][DT];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int mi = 0; mi < DT; ++mi) o[mt][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};  // reference max per row, log2 units
+  f32x4 o[MT][DT];
+  float m[MT];  // reference max per row, log2 units
   // Row sums of the weights, accumulated by the matrix core as ones . P^T
   // from the same bf16 P that multiplies V: every element of lsum[mt] holds
   // the running sum of row hl.
-  f32x4 lsum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 lsum[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int mi = 0; mi < DT; ++mi) o[mt][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[mt] = -INFINITY;
+    lsum[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
   const int last_blk = (kv_end - 1) / kBlock;  // last block any row reads
@@ -343,9 +354,9 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     constexpr bool kSplit = decltype(split_tag)::value;
     const uint8_t* kst = ks[stage];
     const uint8_t* vst = vs[stage];
-    f32x4 st[2][NS];
+    f32x4 st[MT][NS];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int n = 0; n < NS; ++n) st[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -353,13 +364,13 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
         const bf16x8 a = as_bf16x8(*(const u32x4*)(kst + n * 16 * RB + koff[i]));
-        st[0][n] = mfma_16x16x32(a, qv[0][i], st[0][n]);
-        st[1][n] = mfma_16x16x32(a, qv[1][i], st[1][n]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) st[mt][n] = mfma_16x16x32(a, qv[mt][i], st[mt][n]);
       }
     }
     if (masked) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int n = 0; n < NS; ++n)
 #pragma unroll
@@ -372,10 +383,10 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     // its scores exceeds the current reference by more than 2^kLazyP.
     // NaN-propagating maximum (masked scores are already -inf): needs no
     // canonicalisation of the MFMA results and maps to 3-input maxima.
-    float lmax[2];
+    float lmax[MT];
     bool over = false;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       float va = st[mt][0][0], vb = st[mt][0][1];
 #pragma unroll
       for (int i = 2; i < 4 * NS; i += 2) {
@@ -388,7 +399,7 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     }
     if (__any(over)) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const float mn = fmaxf(m[mt], max_across_groups(lmax[mt]));
         const float alpha = fast_exp2(m[mt] - mn);
         lsum[mt] *= alpha;
@@ -398,7 +409,7 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
       }
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const float negm = -m[mt];
 #pragma unroll
       for (int n = 0; n < NS; ++n)
@@ -411,9 +422,9 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     // reads), matching the order in which P^T is packed from S^T.
 #pragma unroll
     for (int kp = 0; kp < NS / 2; ++kp) {
-      bf16x8 pb[2], pl[2];
+      bf16x8 pb[MT], pl[MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         if constexpr (kSplit) {
           u32x4 hv, lv;
 #pragma unroll
@@ -441,15 +452,15 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
         const i16x4 a1 = lds_read_tr16((const uint16_t*)(va + 16 * RB));
         const bf16x8 av = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][mi] = mfma_16x16x32(av, pb[0], o[0][mi]);
-        o[1][mi] = mfma_16x16x32(av, pb[1], o[1][mi]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt][mi] = mfma_16x16x32(av, pb[mt], o[mt][mi]);
         if constexpr (kSplit) {
-          o[0][mi] = mfma_16x16x32(av, pl[0], o[0][mi]);
-          o[1][mi] = mfma_16x16x32(av, pl[1], o[1][mi]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) o[mt][mi] = mfma_16x16x32(av, pl[mt], o[mt][mi]);
         }
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         lsum[mt] = mfma_16x16x32(ones, pb[mt], lsum[mt]);
         if constexpr (kSplit) lsum[mt] = mfma_16x16x32(ones, pl[mt], lsum[mt]);
       }
@@ -499,8 +510,8 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     // partition q0 (the chunk) of rows s + tl: unnormalised numerator,
     // reference max (log2 units) and weight sum
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int row = w * 32 + mt * 16 + hl;
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = w * RW + mt * 16 + hl;
       const int tl = row / G;
       const int hh = row % G;
       if (tl >= nq) continue;
@@ -513,9 +524,9 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : kWavesA) * kWave, 1) vo
     return;
   }
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const float ltot = lsum[mt][0];
-    const int row = w * 32 + mt * 16 + hl;
+    const int row = w * RW + mt * 16 + hl;
     const int tl = row / G;
     const int hh = row % G;
     if (tl >= nq) continue;
@@ -610,7 +621,7 @@ hipError_t launch_tiles_d(const ForwardArgs& a, const PrefillPlan& p, hipStream_
 
 template <int D, int G>
 hipError_t launch_prefix_g(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream) {
-  constexpr int BQ = 32 * kWavesA / G;
+  constexpr int BQ = 16 * kRowTiles * kWavesP / G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   PrefixArgs x{p.ws_o, p.ws_ml, p.num_parts_max, p.chunk_keys, p.prefix_keys, a.num_seqs,
                (a.num_seqs + BQ - 1) / BQ, p.chunks, a.num_tokens};
@@ -619,7 +630,7 @@ hipError_t launch_prefix_g(const ForwardArgs& a, const PrefixPlan& p, hipStream_
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   profile_begin(PA_KERNEL_PREFIX, stream);
   hipLaunchKernelGGL((prefill_tile_kernel<D, G, kPrefix>), dim3((unsigned)grid),
-                     dim3(kWavesA * kWave), 0, stream, (const uint16_t*)a.q,
+                     dim3(kWavesP * kWave), 0, stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_table,
                      a.seq_lens, a.query_start_loc, (uint16_t*)a.out, nullptr, nullptr,
                      scale_log2, a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, 0, x);
@@ -653,11 +664,12 @@ hipError_t launch_prefix(const ForwardArgs& a, const PrefixPlan& p, hipStream_t 
   }
 }
 
-int32_t prefill_tile_queries(int32_t group) { return 32 * kWavesA / group; }
-int32_t prefill_split_tile_queries(int32_t group) { return 32 * kWavesB / group; }
+int32_t prefill_tile_queries(int32_t group) { return 16 * kRowTilesA * kWavesA / group; }
+int32_t prefill_split_tile_queries(int32_t group) { return 16 * kRowTiles * kWavesB / group; }
+int32_t prefix_tile_rows(int32_t group) { return 16 * kRowTiles * kWavesP / group; }
 
 int32_t prefill_split_tiles_per_row(int32_t group) {
-  const int32_t bq = 32 * kWavesB / group;
+  const int32_t bq = 16 * kRowTiles * kWavesB / group;
   return (kSplitKeys + bq - 1) / bq;
 }
 
