@@ -235,9 +235,9 @@ int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mappi
  * attended once for all rows together: their query tokens are stacked as
  * the rows of matrix-core tiles (G heads each), chunk by chunk of the
  * prefix, leaving partial results per row; each row's own blocks after the
- * prefix run on the partitioned decode schedule; a merge pass combines both
- * (the log-sum-exp identity). Results agree with pa_forward_ex to rounding
- * order.
+ * prefix run on the partitioned decode schedule, whose last workgroup per
+ * (row, KV head) merges both (the log-sum-exp identity). Results agree with
+ * pa_forward_ex to rounding order.
  *
  *   q ... out, sizes, num_blocks   as for pa_forward_ex, with num_tokens =
  *                    num_seqs: every row is a decode row (query_start_loc
@@ -246,7 +246,10 @@ int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mappi
  *                    row 0's entries are the ones read
  *   max_seq_len_hint as for pa_forward_ex; must exceed 16 * prefix_blocks
  *   workspace        >= pa_shared_prefix_workspace_bytes(...) bytes, 16-byte
- *                    aligned; scratch written before it is read
+ *                    aligned; its first PA_WORKSPACE_COUNTER_BYTES must be
+ *                    zero before its first use (every call leaves them
+ *                    zero), the rest is scratch written before it is read;
+ *                    calls sharing a workspace must be ordered on one stream
  *   flags            0 or PA_FORWARD_SHARED_BLOCKS
  *
  * Caller contract (not checked): every row's first prefix_blocks table

@@ -582,14 +582,14 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
 // into the caches at slot_mapping[qsl[s]]: the workgroup of the row's last
 // partition writes its KV head's slice, and every workgroup reads that token
 // from knew / vnew.
-template <int D, int NBUF, bool kStreamV, bool kWrite>
+template <int D, int NBUF, bool kStreamV, bool kWrite, bool kHeads>
 __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     float scale_log2, int32_t Hq, int32_t Hkv, int32_t G, int32_t MB, int32_t part_tokens,
-    int32_t num_parts_max, int32_t tok_base, int32_t part_base, int32_t QM,
+    int32_t num_parts_max, int32_t tok_base, int32_t part_base, int32_t QM, int32_t HG,
     int32_t* __restrict__ counters, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, const int64_t* __restrict__ slot_mapping,
     uint16_t* k_cache_w, uint16_t* v_cache_w) {
@@ -602,18 +602,24 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
   const int W = blockDim.x / kWave;
   // Rows vary fastest in the grid: consecutive workgroups are dealt to the
   // XCDs in turn, so the work of every partition index and head spreads
-  // over all XCDs.
+  // over all XCDs. A workgroup holds HG KV heads (HG divides W): wave w
+  // takes head w % HG of them and every (W / HG)-th block of the partition
+  // from block w / HG on.
+  // (kHeads: HG > 1 heads per workgroup; otherwise HG is 1 and the
+  // instantiation keeps the index arithmetic free of divisions)
   const int s = blockIdx.x;
-  const int g = blockIdx.y;
+  const int sub = kHeads ? w / HG : w;
+  const int Wsub = kHeads ? W / HG : W;
+  const int g = kHeads ? blockIdx.y * HG + w % HG : blockIdx.y;
   const int part = blockIdx.z;
-  // Block ids of this wave (lane k: partition block w + k*W), read before
-  // the row's length is known so the loads overlap; the index is kept inside
-  // the row, and lanes past the wave's blocks are never used.
+  // Block ids of this wave (lane k: partition block sub + k*Wsub), read
+  // before the row's length is known so the loads overlap; the index is
+  // kept inside the row, and lanes past the wave's blocks are never used.
   // Keys from tok_base on (a multiple of 16: after a shared-prefix pass the
   // prefix's partials are already in the workspace).
   const int bpp = part_tokens / kBlock;
   const int b_begin = tok_base / kBlock + part * bpp;
-  const int jb = w + lane * W;
+  const int jb = sub + lane * Wsub;
   const int my_blk = (jb < bpp && b_begin + jb < MB)
                          ? block_table[(int64_t)s * MB + b_begin + jb] : 0;
   // Workgroup-uniform exits (before any barrier).
@@ -633,7 +639,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
   const int tok_end = min(L, tok_begin + part_tokens);
   const int nparts = (L - tok_base + part_tokens - 1) / part_tokens;
   const int nblk = (tok_end + kBlock - 1) / kBlock - b_begin;
-  const int nmine = nblk > w ? (nblk - 1 - w) / W + 1 : 0;  // blocks of this wave
+  const int nmine = nblk > sub ? (nblk - 1 - sub) / Wsub + 1 : 0;  // blocks of this wave
   const int hl = lane & 15;
   const int grp = lane >> 4;
   const int64_t kv_row = (int64_t)Hkv * D;
@@ -669,13 +675,13 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
       load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
     const int col_lim = L - ql + min(hl, ncols - 1) / G;  // last key of the lane's column
     stream_blocks<D, NBUF, kStreamV, kWrite>(
-        acc, qv, my_blk, nmine, (b_begin + w) * kBlock, W * kBlock, tok_end,
+        acc, qv, my_blk, nmine, (b_begin + sub) * kBlock, Wsub * kBlock, tok_end,
         k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row, v_cache + (int64_t)g * D,
         kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt, col_lim);
     acc.lsum = sum_across_groups(acc.lsum);
   }
   if constexpr (kWrite) {
-    if (part == nparts - 1 && w == 0) {  // wave-uniform
+    if (part == nparts - 1 && sub == 0) {  // wave-uniform
       // [NB, 16, Hkv, D]: the slot's row starts at element slot * Hkv * D
       const int64_t slot = first_lane64(nt.slot);
       if constexpr (!kEarly) wval = new_token_data();
@@ -686,13 +692,60 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
   }
 
   // With counters, the workgroup that finishes a split row last merges its
-  // partials (no combine launch): partials go past this XCD's L2.
+  // partials (no combine launch): partials go past this XCD's L2. A row
+  // whose own keys fit this one partition after partials 0 .. part_base-1
+  // left by an earlier launch (the shared-prefix pass) merges those with
+  // its state directly, in the same order, with no hand-over.
   const bool split = nparts > 1 || part_base > 0;
-  merge_waves<D>(acc, (float*)lds, W, 1, ncols, w, lane,
-                 [&](int, int col, int d, float M, float den, float n0, float n1) {
+  const bool direct = counters && nparts == 1 && part_base > 0;
+  const int64_t pstride = (int64_t)QM * Hq;
+  // Online merge in partition order of partials c_lo .. c_hi-1 of (token
+  // tk, head qh) into (M, den, n0, n1) at d, d+1; eight loads in flight.
+  auto merge_partials = [&](int c_lo, int c_hi, int tk, int qh, int d, float& M, float& den,
+                            float& n0, float& n1) {
+    const int64_t row0 = (int64_t)s * num_parts_max * pstride + (int64_t)tk * Hq + qh;
+    for (int c0 = c_lo; c0 < c_hi; c0 += 8) {
+      f32x2 ml[8], ov[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t r = row0 + min(c0 + k, c_hi - 1) * pstride;
+        ml[k] = load_coherent2(ws_ml + r * 2);
+        ov[k] = load_coherent2(ws_o + r * D + d);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // a partition where the column saw no visible key adds nothing
+        if (c0 + k < c_hi && ml[k][0] != -INFINITY) {
+          const float mn = fmaxf(M, ml[k][0]);
+          const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+          const float e = fast_exp2(ml[k][0] - mn);
+          den = den * sc + e * ml[k][1];
+          n0 = n0 * sc + e * ov[k][0];
+          n1 = n1 * sc + e * ov[k][1];
+          M = mn;
+        }
+      }
+    }
+  };
+  auto merged = [&](int sl, int col, int d, float M, float den, float n0, float n1) {
     const int tk = col / G;
-    const int qh = g * G + col % G;
-    if (!split) {
+    const int qh = (blockIdx.y * HG + sl) * G + col % G;
+    if (!split || direct) {
+      if (direct) {
+        float Mx = -INFINITY, dx = 0.f, x0 = 0.f, x1 = 0.f;
+        merge_partials(0, part_base, tk, qh, d, Mx, dx, x0, x1);
+        if (M != -INFINITY) {  // this partition's state comes last
+          const float mn = fmaxf(Mx, M);
+          const float sc = Mx == -INFINITY ? 0.f : fast_exp2(Mx - mn);
+          const float e = fast_exp2(M - mn);
+          dx = dx * sc + e * den;
+          x0 = x0 * sc + e * n0;
+          x1 = x1 * sc + e * n1;
+        }
+        den = dx;
+        n0 = x0;
+        n1 = x1;
+      }
       const float inv = 1.0f / den;
       *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) =
           pack_bf16x2(n0 * inv, n1 * inv);
@@ -707,10 +760,11 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
         if (d == 0) *(f32x2*)(ws_ml + base * 2) = f32x2{M, den};
       }
     }
-  });
-  if (!counters || !split) return;
+  };
+  merge_waves<D>(acc, (float*)lds, W, kHeads ? HG : 1, ncols, w, lane, merged);
+  if (!counters || !split || direct) return;
   // Publish: this workgroup's partial stores have completed before it counts
-  // itself in; the last of the row's nparts workgroups (of this KV head)
+  // itself in; the last of the row's nparts workgroups (of these KV heads)
   // merges partials 0 .. part_base + nparts - 1 in order and leaves the
   // counter at zero for the next call.
   int32_t* flag = (int32_t*)lds;
@@ -720,7 +774,7 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
   // maximum is a caller error, and the counter still returns to zero)
   const int nrun = min(nparts, (int)gridDim.z);
   if (threadIdx.x == 0) {
-    int32_t* ctr = counters + (int64_t)s * Hkv + g;
+    int32_t* ctr = counters + (int64_t)s * Hkv + blockIdx.y * HG;
     const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == nrun - 1;
     if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -729,36 +783,14 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
   __syncthreads();
   if (!*flag) return;
   const int np = part_base + nrun;
-  const int64_t pstride = (int64_t)QM * Hq;
-  for (int idx = threadIdx.x; idx < ncols * (D / 2); idx += blockDim.x) {
-    const int col = idx / (D / 2);
+  const int per_head = ncols * (D / 2);
+  for (int idx = threadIdx.x; idx < HG * per_head; idx += blockDim.x) {
+    const int col = (idx % per_head) / (D / 2);
     const int d = 2 * (idx % (D / 2));
     const int tk = col / G;
-    const int qh = g * G + col % G;
-    const int64_t row0 = (int64_t)s * num_parts_max * pstride + (int64_t)tk * Hq + qh;
+    const int qh = (blockIdx.y * HG + idx / per_head) * G + col % G;
     float M = -INFINITY, den = 0.f, n0 = 0.f, n1 = 0.f;
-    for (int c0 = 0; c0 < np; c0 += 8) {
-      f32x2 ml[8], ov[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int64_t r = row0 + min(c0 + k, np - 1) * pstride;
-        ml[k] = load_coherent2(ws_ml + r * 2);
-        ov[k] = load_coherent2(ws_o + r * D + d);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        // a partition where the column saw no visible key adds nothing
-        if (c0 + k < np && ml[k][0] != -INFINITY) {
-          const float mn = fmaxf(M, ml[k][0]);
-          const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mn);
-          const float e = fast_exp2(ml[k][0] - mn);
-          den = den * sc + e * ml[k][1];
-          n0 = n0 * sc + e * ov[k][0];
-          n1 = n1 * sc + e * ov[k][1];
-          M = mn;
-        }
-      }
-    }
+    merge_partials(0, np, tk, qh, d, M, den, n0, n1);
     const float inv = 1.0f / den;
     *(uint32_t*)(out + ((int64_t)(t0 + tk) * Hq + qh) * D + d) = pack_bf16x2(n0 * inv, n1 * inv);
   }
@@ -861,26 +893,28 @@ hipError_t launch_decode_nb(const ForwardArgs& a, const DecodePlan& p, hipStream
     profile_end(PA_KERNEL_DECODE, stream);
     return hipGetLastError();
   }
-  dim3 grid(a.num_seqs, a.num_kv_heads, p.num_parts_max - p.part_base);
+  dim3 grid(a.num_seqs, a.num_kv_heads / p.heads_per_wg, p.num_parts_max - p.part_base);
   const size_t lds = (size_t)p.waves * Sh::kLdsWave * sizeof(uint16_t);
   profile_begin(PA_KERNEL_DECODE, stream);
   if (p.fused_write) {
-    hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, true>), grid, dim3(p.waves * kWave), lds,
+    hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, true, false>), grid, dim3(p.waves * kWave), lds,
                        stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       p.tok_base, p.part_base, p.qmax,
+                       p.tok_base, p.part_base, p.qmax, p.heads_per_wg,
                        p.fused_combine ? p.counters : nullptr, (const uint16_t*)p.knew,
                        (const uint16_t*)p.vnew,
                        p.slot_mapping, (uint16_t*)p.k_cache_w, (uint16_t*)p.v_cache_w);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, NBUF, kStreamV, false>), grid, dim3(p.waves * kWave),
+    auto kernel = p.heads_per_wg > 1 ? decode_kernel<D, NBUF, kStreamV, false, true>
+                                     : decode_kernel<D, NBUF, kStreamV, false, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(p.waves * kWave),
                        lds, stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                        (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.query_start_loc,
                        (uint16_t*)a.out, p.ws_o, p.ws_ml, scale_log2, a.num_q_heads,
                        a.num_kv_heads, G, a.max_blocks_per_seq, p.part_tokens, p.num_parts_max,
-                       p.tok_base, p.part_base, p.qmax,
+                       p.tok_base, p.part_base, p.qmax, p.heads_per_wg,
                        p.fused_combine ? p.counters : nullptr, nullptr, nullptr, nullptr,
                        nullptr, nullptr);
   }
@@ -916,8 +950,8 @@ size_t decode_stream_lds_bytes(int32_t head_size, int32_t waves, int32_t num_seq
 hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t stream) {
   const int maxw = decode_max_waves(a.head_size, p.prefetch, p.fused_write);
   if (p.waves < 1 || p.waves > maxw || a.num_kv_heads > 65535) return hipErrorInvalidValue;
-  if (p.fused_write && (p.stream || !p.knew || !p.vnew || !p.slot_mapping || !p.k_cache_w ||
-                        !p.v_cache_w))
+  if (p.fused_write && (p.stream || p.heads_per_wg != 1 || !p.knew || !p.vnew ||
+                        !p.slot_mapping || !p.k_cache_w || !p.v_cache_w))
     return hipErrorInvalidValue;
   if (p.tok_base < 0 || p.tok_base % kBlock || p.part_base < 0 ||
       p.num_parts_max - p.part_base < 1 || ((p.tok_base || p.part_base) && p.stream))
@@ -930,8 +964,10 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
     if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||
         decode_stream_lds_bytes(a.head_size, p.waves, a.num_seqs) > 64 * 1024)
       return hipErrorInvalidValue;
-  } else if (p.part_tokens <= 0 || p.part_tokens % kBlock ||
-             p.part_tokens / kBlock > kWave * p.waves || p.num_parts_max > 65535) {
+  } else if (p.heads_per_wg < 1 || a.num_kv_heads % p.heads_per_wg ||
+             p.waves % p.heads_per_wg || p.part_tokens <= 0 || p.part_tokens % kBlock ||
+             p.part_tokens / kBlock > kWave * (p.waves / p.heads_per_wg) ||
+             p.num_parts_max > 65535) {
     return hipErrorInvalidValue;
   }
   // Ring depths that fit the register budget without spills: 2 or 3 blocks

@@ -51,6 +51,7 @@ struct DecodePlan {
   int32_t part_tokens;    // partitioned: tokens per partition (multiple of 16)
   int32_t num_parts_max;  // partitioned: partitions per row (grid z; workspace stride)
   int32_t waves;          // waves per workgroup (1..decode_max_waves)
+  int32_t heads_per_wg;   // partitioned: KV heads per workgroup (divides Hkv and waves)
   int32_t prefetch;       // register ring depth in 16-token blocks (2, or 3 at D = 64)
   bool stream_v;          // V through nontemporal loads (blocks not shared)
   float* ws_o;            // partial outputs: stream [wgs][2][Hq][D], partitioned [S][parts][Hq][D]

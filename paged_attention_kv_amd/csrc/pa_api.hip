@@ -411,6 +411,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   dp.num_parts_max = w.num_parts_max;
   dp.prefetch = w.prefetch;
   dp.waves = dp.stream ? w.stream_waves : w.waves;
+  dp.heads_per_wg = 1;
   dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
   dp.ws_o = (float*)(ws + w.off_o);
   dp.ws_ml = (float*)(ws + w.off_ml);
@@ -478,8 +479,8 @@ namespace {
 // blocks of every row in chunks; each row's remaining keys run on the
 // partitioned decode schedule; the combine merges both.
 struct PrefixLayout {
-  int32_t chunks, chunk_keys, prefix_keys, waves, prefetch, part_tokens, suffix_parts,
-      num_parts_max;
+  int32_t chunks, chunk_keys, prefix_keys, waves, prefetch, heads_per_wg, part_tokens,
+      suffix_parts, num_parts_max;
   size_t off_o, off_ml, total;
 };
 // Prefix workgroups aimed for: one per CU; chunks of at least 512 keys.
@@ -508,9 +509,25 @@ bool plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, in
   p.chunk_keys = (int32_t)(((p.prefix_keys + chunks - 1) / chunks + 63) / 64 * 64);
   p.chunks = (p.prefix_keys + p.chunk_keys - 1) / p.chunk_keys;
   p.prefetch = decode_prefetch(head_size);
-  p.waves = decode_waves(head_size, p.prefetch);
+  // The rows' own blocks after the prefix are few per row: one workgroup
+  // per row holds all its KV heads (the largest divisor of Hkv that fits,
+  // one wave each), instead of a workgroup per (row, KV head) whose waves
+  // would each stream one or two blocks. PA_PREFIX_SUFFIX_HEADS=1 restores
+  // a workgroup per KV head with the usual waves (for comparisons).
+  static const int one_head = env_int("PA_PREFIX_SUFFIX_HEADS", 0, 1, 0);
+  if (one_head) {
+    p.heads_per_wg = 1;
+    p.waves = decode_waves(head_size, p.prefetch);
+  } else {
+    const int32_t maxw = std::max(1, pa::decode_max_waves(head_size, p.prefetch));
+    int32_t hg = std::min(num_kv_heads, maxw);
+    while (num_kv_heads % hg) --hg;
+    p.heads_per_wg = hg;
+    p.waves = hg;
+  }
   const int32_t suffix_len = max_len - p.prefix_keys;
-  p.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, p.waves, suffix_len);
+  p.part_tokens = choose_part_tokens(num_seqs, num_kv_heads / p.heads_per_wg,
+                                     p.waves / p.heads_per_wg, suffix_len);
   p.suffix_parts = (suffix_len + p.part_tokens - 1) / p.part_tokens;
   p.num_parts_max = p.chunks + p.suffix_parts;
   if (p.suffix_parts > kMaxGridZ) return false;
@@ -622,6 +639,7 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   dp.part_tokens = pl.part_tokens;
   dp.num_parts_max = pl.num_parts_max;
   dp.waves = pl.waves;
+  dp.heads_per_wg = pl.heads_per_wg;
   dp.prefetch = pl.prefetch;
   dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
   dp.ws_o = pp.ws_o;
@@ -629,7 +647,11 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   dp.tok_base = pl.prefix_keys;
   dp.part_base = pl.chunks;
   dp.qmax = 1;
-  dp.fused_combine = false;
+  // The last workgroup of each (row, KV head) merges the prefix chunks'
+  // partials with its own row's (no combine launch), through the counters at
+  // the start of the workspace.
+  dp.counters = (int32_t*)ws;
+  dp.fused_combine = decode_fused_combine(num_seqs, num_kv_heads);
   e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix decode launch");
   return PA_OK;

@@ -283,7 +283,8 @@ def test_shared_prefix_workload_sampled_rows():
     pa.profile_begin()
     out = shared_prefix_call(case, spec.shared_prefix_blocks).clone()
     per = pa.profile_end()
-    assert per["prefix"][0] == 1 and per["decode"][0] == 1 and per["combine"][0] == 1, per
+    # the decode launch merges the prefix chunks' partials itself
+    assert per["prefix"][0] == 1 and per["decode"][0] == 1 and "combine" not in per, per
     pick = sorted(random.Random(15).sample(range(256), 14) + [0, 255])
     rows, want = oracle_rows(case, pick)
     assert_close(out.cpu()[rows], want, "shared prefix")
