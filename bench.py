@@ -472,7 +472,7 @@ def main(argv=None):
                                      "set and replayed (value uses eager launches)"},
             "block_table_rotations": d["rotations"],
             "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
-        kname = "decode_kernel<64, 2, true, %s>" % ("true" if d["fused"] else "false")
+        kname = "decode_kernel<64, 2, true, %s, false>" % ("true" if d["fused"] else "false")
         line["roofline"] = {"bound": "hbm", "kernel": kname,
                             "achieved": round(d["kernel_gbs"], 2), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
