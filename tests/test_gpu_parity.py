@@ -659,3 +659,22 @@ def test_read_probe_only_reads(waves, per_wg):
     torch.cuda.synchronize()
     assert int(sink.item()) in (0, 0x9E3779B9 - (1 << 32))
     assert torch.equal(case.k_cache[:4096], kc0) and torch.equal(case.v_cache[-4096:], vc0)
+
+
+def test_empty_batch_is_a_no_op():
+    """No tokens at all (every row's q_len is 0, or no rows): the calls
+    launch nothing and return an empty output; the cache is untouched."""
+    spec = wl.custom("empty_rows", 32, 8, 128, rows=[(0, 40), (0, 17)], seed=160)
+    case = wl.make_case(spec, device=DEV)
+    kc0 = case.k_cache.clone()
+    pa.profile_begin()
+    out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
+                               case.q, case.block_table, case.seq_lens, case.query_start_loc,
+                               case.scale)
+    out2 = pa.forward(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                      case.query_start_loc, case.scale)
+    torch.cuda.synchronize()
+    per = pa.profile_end()
+    assert out.shape[0] == 0 and out2.shape[0] == 0
+    assert sum(n for n, _ in per.values()) == 0, per
+    assert torch.equal(case.k_cache, kc0)
