@@ -442,6 +442,12 @@ def main(argv=None):
                     "tokens_per_s": round(spec.num_tokens / (ms2 * 1e-3), 1)}
             if i == 4:
                 entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                pms, pshape, pbytes = run_read_probe(pa, inp, max(5, args.steps // 5), 2)
+                pgbs = pbytes / (pms * 1e-3) / 1e9
+                entry["read_probe"] = {"us": round(pms * 1e3, 3), "gbs": round(pgbs, 1),
+                                       "waves_blocks_per_wg": list(pshape),
+                                       "forward_frac_of_probe": round(b / (ms_fwd * 1e-3) / 1e9
+                                                                      / pgbs, 4)}
             if name == "spec_decode":
                 entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                 # the same rows without the tight hint: the prefill path
