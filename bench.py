@@ -264,12 +264,18 @@ def sub_spec(spec, rows, name):
 # ---------------------------------------------------------------------------
 
 def decode_source_hash() -> str:
-    """Hash of the decode kernel's sources (decode.hip and common.h)."""
+    """Hash of the decode kernel's code (decode.hip and common.h with their
+    comments removed and white space collapsed, so that an edit of a comment
+    does not count as a change of the kernel)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("decode.hip", "common.h"):
-        with open(os.path.join(ROOT, "paged_attention_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_attention_kv_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -284,7 +290,7 @@ def measured_traffic(kernel: str, workload: str):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("decode_src_sha256_16") != decode_source_hash():
+    if rec.get("decode_code_sha256_16") != decode_source_hash():
         return None
     for key, k in rec.get("kernels", {}).items():
         name, _, wl = key.partition(" @ ")

@@ -38,9 +38,12 @@
 //    device-coherent stores and count themselves in on a per-row counter.
 //    (Row lengths are read on the device; the host never sees them.)
 //  * partitioned (decode_kernel): one workgroup per (row, KV head, fixed-size
-//    partition), W waves taking the partition's blocks in turn; rows of more
-//    than one partition are merged by decode_combine_kernel. Used when the
-//    batch has too many rows for the stream kernel's per-workgroup row scan.
+//    partition) -- or per (row, partition) holding several KV heads -- with
+//    W waves taking the partition's blocks in turn; the last workgroup of a
+//    row of several partitions merges their partials (arrival counter), or
+//    decode_combine_kernel does after the launch. Used for small batches,
+//    whose even shares would be too short to hide their fixed latency, and
+//    for batches with too many rows for the stream kernel's row scan.
 #include <math.h>
 
 #include "common.h"
