@@ -201,10 +201,12 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
  * pa_forward_ex(q, k_cache, v_cache, ..., flags, stream) (the write feeds the
  * forward pass, section "Prefix Caching"; both per section "Run forward
  * pass"). When max_query_len_hint == 1 (every row is a decode row) and the
- * decode rows take the partitioned schedule, a single launch does both: each
- * row's workgroups write its new token into the caches and read that token
- * from k and v rather than from the slot being written. Otherwise the write
- * is a launch of its own ahead of the forward launches.
+ * decode rows take the partitioned schedule (with at most 8 waves per
+ * workgroup where the head size needs the registers; the default takes 4),
+ * a single launch does both: each row's workgroups write its new token into
+ * the caches and read that token from k and v rather than from the slot
+ * being written. Otherwise the write is a launch of its own ahead of the
+ * forward launches.
  *
  *   k, v, slot_mapping   as for pa_cache_write (k, v: bf16 [num_tokens,
  *                        num_kv_heads, head_size]; slot_mapping int64
