@@ -302,6 +302,9 @@ SHARED_PREFIX_CASES = [
     ("g1_odd", 8, 8, 64, 33, [3, 250, 16]),
     ("g16", 16, 1, 128, 70, [1, 7, 900]),
     ("rows300", 32, 8, 128, 12, [1 + (11 * i) % 50 for i in range(300)]),
+    # 16 KV heads: all of a row's heads in one workgroup at D = 64, eight at D = 128
+    ("h16_d64", 16, 16, 64, 9, [2, 31, 600, 1]),
+    ("h16_d128", 32, 16, 128, 9, [2, 31, 600, 1]),
 ]
 
 
