@@ -2,9 +2,10 @@
 launches) and replayed: every replay, with new inputs copied into the
 captured buffers and eager work in between, gives the same bits as the
 eager call on the same inputs. Covers the fused decode launch, partitioned
-rows with a combine pass, the even-share schedule (its arrival counters are
-reset by the kernels themselves, so replays start from zero), and a mixed
-step with prefill tiles and their device planner."""
+rows merged in the kernel (arrival counters, reset by the kernels
+themselves, so replays start from zero), the even-share schedule, a mixed
+step with prefill tiles and their device planner, rows of four query tokens
+on both decode schedules, and the shared-prefix pass."""
 
 import pytest
 import torch
@@ -22,6 +23,9 @@ CASES = [
     ("decode_long_rows", 64, 8, 128, [(1, 30000), (1, 12000), (1, 5)], "partitioned"),
     ("even_shares", 32, 8, 128, [(1, 2000 + 61 * i) for i in range(200)], "even"),
     ("mixed", 32, 8, 128, [(1, 900), (300, 1000), (1, 33), (64, 0), (1, 4000)], None),
+    # rows of four query tokens (speculative verify) on each decode schedule
+    ("verify_even", 32, 8, 128, [(4, 1500 + 97 * i) for i in range(80)], "even"),
+    ("verify_partitioned", 32, 8, 64, [(4, 300 + 53 * i) for i in range(40)], "partitioned"),
 ]
 
 
@@ -63,3 +67,39 @@ def test_graph_replays_match_eager(name, hq, hkv, d, rows, schedule):
         # eager work between replays
         _ = (q.float() @ q.float()[:1].transpose(1, 2).contiguous()).sum()
     assert int(ws[:pa.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
+
+
+def test_graph_replays_of_the_shared_prefix_pass_match_eager():
+    """The shared-prefix pass (prefix tiles, then the rows' own blocks with
+    the merge in the kernel) captured and replayed with new queries."""
+    pb = 24
+    rows = [(1, 16 * pb + own - 1) for own in (1, 17, 40, 200, 5, 64)]
+    spec = wl.custom("prefix_graph", 32, 8, 128, rows=rows, seed=181, shared_prefix_blocks=pb)
+    print(f"\n[case] graph replay shared-prefix pass: S={spec.num_seqs}", flush=True)
+    case = wl.make_case(spec, device=DEV)
+    pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
+    q = case.q.clone()
+    out = torch.empty_like(q)
+    ms = max(spec.seq_lens)
+
+    def step(o):
+        pa.forward_shared_prefix(q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                 case.query_start_loc, case.scale, pb, out=o, max_seq_len=ms)
+
+    step(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    ref = torch.empty_like(out)
+    for i in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        step(ref)
+        torch.cuda.synchronize()
+        assert torch.isfinite(got.float()).all()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        _ = (q.float() * 2).sum()
