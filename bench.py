@@ -520,7 +520,11 @@ def main(argv=None):
                              "kernel_avg_us": pre["kernels"],
                              "tflops": round(pre["flops"] / (pre["ms_fwd"] * 1e-3) / 1e12, 2),
                              "frac_of_bf16_peak": round(pre["flops"] / (pre["ms_fwd"] * 1e-3)
-                                                        / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                                                        / 1e12 / BF16_PEAK_TFLOPS, 4),
+                             # the tile kernel alone (events around each launch)
+                             "tile_kernel_frac_of_bf16_peak": round(
+                                 pre["flops"] / (pre["kernels"]["prefill"] * 1e-6) / 1e12
+                                 / BF16_PEAK_TFLOPS, 4) if "prefill" in pre["kernels"] else None},
             "decode_rows": {"ms": round(dec["ms_fwd"], 4), "bytes": dec["bytes"],
                             "kernel_avg_us": dec["kernels"],
                             "gbs": round(dec["bytes"] / (dec["ms_fwd"] * 1e-3) / 1e9, 2),
