@@ -51,9 +51,25 @@ def write_and_forward(case, hints=True, **kw):
 
 def oracle_rows(case, seqs, tokens_per_seq=None):
     """Oracle output for the listed sequences (optionally only some of their
-    query rows), computed on a CPU copy of just the blocks they read.
+    query rows), computed on a CPU copy of just the blocks they read. The
+    step's new tokens are written into that copy by the oracle's own
+    ref_cache_write from the seeded k and v (over whatever the library wrote
+    there), so no oracle input comes from the library.
     Returns (flattened row indices, [R, Hq, D] float64)."""
     q, kc, vc, table, lens, qsl, tmap = wl.sequences_subset(case, seqs)
+    bs = case.spec.block_size
+    # the full pool's blocks read by these rows, in the order of the copy
+    bt = case.block_table.cpu()
+    lens_all = case.seq_lens.cpu().tolist()
+    used = torch.unique(torch.cat([bt[sq, :-(-lens_all[sq] // bs)].to(torch.int64)
+                                   for sq in seqs]))
+    slots = case.slot_mapping.cpu()[tmap]
+    keep = slots >= 0
+    blk, off = slots[keep] // bs, slots[keep] % bs
+    pos = torch.searchsorted(used, blk)
+    assert bool((used[pos.clamp(max=len(used) - 1)] == blk).all()), "a new token outside its row"
+    oracle.ref_cache_write(case.k.cpu()[tmap][keep], case.v.cpu()[tmap][keep], pos * bs + off,
+                           kc, vc)
     pick = None
     if tokens_per_seq is not None:
         pick = []
@@ -132,6 +148,28 @@ def test_decode_workload_all_rows(schedule):
     out = write_and_forward(case, decode_schedule=schedule)
     rows, want = oracle_rows(case, list(range(spec.num_seqs)))
     assert_close(out.cpu()[rows], want, "decode")
+
+
+def test_decode_workload_fused_write_and_forward_all_rows():
+    """Workload 2 as the benchmark times it: one pa_write_and_forward call
+    (the write rides in the decode launch) on the default schedule. Every
+    row against the oracle, and the cache rows written bit-exactly."""
+    spec = wl.config(2)
+    banner("workload 2 through pa_write_and_forward (one launch)")
+    case = wl.make_case(spec, device=DEV)
+    pa.profile_begin()
+    out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
+                               case.q, case.block_table, case.seq_lens, case.query_start_loc,
+                               case.scale, max_query_len=1, max_seq_len=max(spec.seq_lens))
+    torch.cuda.synchronize()
+    per = pa.profile_end()
+    assert set(per) == {"decode"} and per["decode"][0] == 1, per
+    kc = case.k_cache.view(-1, spec.num_kv_heads, spec.head_size)
+    vc = case.v_cache.view(-1, spec.num_kv_heads, spec.head_size)
+    assert torch.equal(kc[case.slot_mapping].view(torch.int16), case.k.view(torch.int16))
+    assert torch.equal(vc[case.slot_mapping].view(torch.int16), case.v.view(torch.int16))
+    rows, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_close(out.cpu()[rows], want, "decode, fused write")
 
 
 @pytest.mark.parametrize("schedule", [None, "partitioned"])
