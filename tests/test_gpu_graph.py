@@ -5,7 +5,8 @@ eager call on the same inputs. Covers the fused decode launch, partitioned
 rows merged in the kernel (arrival counters, reset by the kernels
 themselves, so replays start from zero), the even-share schedule, a mixed
 step with prefill tiles and their device planner, rows of four query tokens
-on both decode schedules, and the shared-prefix pass."""
+on both decode schedules, the shared-prefix pass, and several steps
+in one graph."""
 
 import pytest
 import torch
@@ -67,6 +68,51 @@ def test_graph_replays_match_eager(name, hq, hkv, d, rows, schedule):
         # eager work between replays
         _ = (q.float() @ q.float()[:1].transpose(1, 2).contiguous()).sum()
     assert int(ws[:pa.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
+
+
+def test_graph_of_several_steps_matches_eager():
+    """Three decode steps in one graph, each writing its own new tokens into
+    the same slots and attending with its own queries: every replay gives
+    the bits of the three eager steps run in the same order."""
+    rows = [(1, 512 + 37 * i) for i in range(64)]
+    spec = wl.custom("graph_loop", 32, 4, 64, rows=rows, seed=191)
+    print(f"\n[case] graph of three steps: S={spec.num_seqs}", flush=True)
+    case = wl.make_case(spec, device=DEV)
+    hints = dict(max_query_len=1, max_seq_len=max(spec.seq_lens))
+    gen = torch.Generator(device=DEV).manual_seed(11)
+
+    def rnd(t):
+        return torch.randn(t.shape, generator=gen, device=DEV).to(t.dtype)
+
+    ins = [(rnd(case.q), rnd(case.k), rnd(case.v)) for _ in range(3)]
+    outs = [torch.empty_like(case.q) for _ in range(3)]
+
+    def steps(dst):
+        for (q, k, v), o in zip(ins, dst):
+            pa.write_and_forward(k, v, case.slot_mapping, case.k_cache, case.v_cache, q,
+                                 case.block_table, case.seq_lens, case.query_start_loc,
+                                 case.scale, out=o, **hints)
+
+    steps(outs)  # kernels loaded and the workspace allocated outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps(outs)
+    refs = [torch.empty_like(case.q) for _ in range(3)]
+    for r in range(3):
+        for q, k, v in ins:
+            q.copy_(rnd(q))
+            k.copy_(rnd(k))
+            v.copy_(rnd(v))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        steps(refs)
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.isfinite(got[i].float()).all()
+            assert torch.equal(got[i].view(torch.int16), refs[i].view(torch.int16)), (r, i)
+        _ = (case.q.float() @ case.q.float()[:1].transpose(1, 2).contiguous()).sum()
 
 
 def test_graph_replays_of_the_shared_prefix_pass_match_eager():
