@@ -198,7 +198,6 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWave
   constexpr int KC = D / 32;                  // QK MFMAs per 16x16 S tile
   constexpr int DT = D / 16;                  // PV output tiles along d
   constexpr int NS = BN / 16;                 // 16-key sub-tiles per tile
-  constexpr int CPR = D / 8;                  // 16-byte chunks per K/V row
   constexpr int NDMA = BN * RB / 1024 / NW;   // 1 KiB load-to-LDS ops per wave per tile (K; V alike)
   static_assert(NDMA * NW * 1024 == BN * RB, "tile must split evenly");
   static_assert(NST == 2 || NST == 3, "stage count");
