@@ -95,6 +95,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Device-coherent store and load of 8 bytes (agent scope, relaxed): they go
 // past this XCD's L2, so workgroups on different XCDs can hand data over.
+// The order that makes the hand-over correct comes from count_in below.
 __device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
   const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
   __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -103,6 +104,30 @@ __device__ __forceinline__ f32x2 load_coherent2(const float* p) {
   const uint64_t v =
       __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
+
+// Hand-over of a split row between workgroups (every thread of the
+// workgroup calls it, after storing its partials with store_coherent2):
+// the stores are released at agent scope by the arrival counter's
+// read-modify-write (each wave first waits for its own stores, then the
+// workgroup barrier orders them before thread 0's release), and the
+// workgroup that arrives last (old value ncontrib - 1) acquires them with
+// the same read-modify-write and an agent-scope acquire fence in every
+// thread before it reads other workgroups' partials. The last arriver resets
+// the counter to zero. Returns true in every thread of the last workgroup.
+__device__ __forceinline__ bool count_in(int32_t* ctr, int ncontrib, int32_t* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == ncontrib - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  const bool last = *flag != 0;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
 }
 
 // Online-softmax state of one wave: O^T tiles (lane: d = 16*mi + 4*(l/16) + r,
@@ -518,20 +543,10 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
     });
 
     if (ncontrib > 1) {
-      // Publish: this workgroup's partial stores have completed before it
-      // counts itself in; the last to count in merges every share's partial
-      // in share order and leaves the counter at zero for the next call.
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        int32_t* ctr = counters + (int64_t)s * gridDim.y + blockIdx.y;
-        const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == ncontrib - 1;
-        if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *flag = last;
-      }
-      __syncthreads();
-      if (*flag) {
+      // Publish and hand over: see count_in. The last to count in merges
+      // every share's partial in share order and leaves the counter at zero
+      // for the next call.
+      if (count_in(counters + (int64_t)s * gridDim.y + blockIdx.y, ncontrib, flag)) {
         // Online merge in share order, eight shares' loads in flight at a
         // time. A share whose blocks hold no key visible to a column (the
         // few keys past an earlier token of a several-token row) left
@@ -766,25 +781,14 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
   };
   merge_waves<D>(acc, (float*)lds, W, kHeads ? HG : 1, ncols, w, lane, merged);
   if (!counters || !split || direct) return;
-  // Publish: this workgroup's partial stores have completed before it counts
-  // itself in; the last of the row's nparts workgroups (of these KV heads)
-  // merges partials 0 .. part_base + nparts - 1 in order and leaves the
-  // counter at zero for the next call.
-  int32_t* flag = (int32_t*)lds;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Publish and hand over (count_in): the last of the row's nparts
+  // workgroups (of these KV heads) merges partials 0 .. part_base + nparts
+  // - 1 in order and leaves the counter at zero for the next call.
   // (partitions past the grid do not run: a length past the planned
   // maximum is a caller error, and the counter still returns to zero)
   const int nrun = min(nparts, (int)gridDim.z);
-  if (threadIdx.x == 0) {
-    int32_t* ctr = counters + (int64_t)s * Hkv + blockIdx.y * HG;
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == nrun - 1;
-    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = last;
-  }
-  __syncthreads();
-  if (!*flag) return;
+  // (the merge stage's LDS is free again after count_in's first barrier)
+  if (!count_in(counters + (int64_t)s * Hkv + blockIdx.y * HG, nrun, (int32_t*)lds)) return;
   const int np = part_base + nrun;
   const int per_head = ncols * (D / 2);
   for (int idx = threadIdx.x; idx < HG * per_head; idx += blockDim.x) {

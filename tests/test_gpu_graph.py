@@ -1,8 +1,10 @@
 """A step captured in a HIP graph (torch.cuda.CUDAGraph over the library's
 launches) and replayed: every replay, with new inputs copied into the
 captured buffers and eager work in between, gives the same bits as the
-eager call on the same inputs. Covers the fused decode launch, partitioned
-rows merged in the kernel (arrival counters, reset by the kernels
+eager call on the same inputs, and matches the oracle on them (whose inputs
+are a CPU copy of the rows' blocks taken before the library was called, the
+replay's own q, k and v written into it by the oracle). Covers the fused
+decode launch, partitioned rows merged in the kernel (arrival counters, reset by the kernels
 themselves, so replays start from zero), the even-share schedule, a mixed
 step with prefill tiles and their device planner, rows of four query tokens
 on both decode schedules, the shared-prefix pass, and several steps
@@ -13,6 +15,7 @@ import torch
 
 import paged_attention_kv_amd as pa
 import workloads as wl
+from oracle_view import OracleView, assert_close
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +38,7 @@ def test_graph_replays_match_eager(name, hq, hkv, d, rows, schedule):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=170 + len(rows))
     print(f"\n[case] graph replay {name}: S={spec.num_seqs} T={spec.num_tokens}", flush=True)
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     hints = dict(max_query_len=max(spec.q_lens), max_seq_len=max(spec.seq_lens))
     ws = torch.zeros(pa.forward_workspace_bytes(spec.num_tokens, spec.num_seqs, hq, hkv, d,
                                                 spec.max_blocks_per_seq, **hints),
@@ -65,6 +69,8 @@ def test_graph_replays_match_eager(name, hq, hkv, d, rows, schedule):
         torch.cuda.synchronize()
         assert torch.isfinite(got.float()).all()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        r, want = view.expect(q=q, k=k, v=v)
+        assert_close(got.cpu()[r], want, f"{name} replay {i}")
         # eager work between replays
         _ = (q.float() @ q.float()[:1].transpose(1, 2).contiguous()).sum()
     assert int(ws[:pa.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
@@ -78,6 +84,7 @@ def test_graph_of_several_steps_matches_eager():
     spec = wl.custom("graph_loop", 32, 4, 64, rows=rows, seed=191)
     print(f"\n[case] graph of three steps: S={spec.num_seqs}", flush=True)
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     hints = dict(max_query_len=1, max_seq_len=max(spec.seq_lens))
     gen = torch.Generator(device=DEV).manual_seed(11)
 
@@ -112,6 +119,9 @@ def test_graph_of_several_steps_matches_eager():
         for i in range(3):
             assert torch.isfinite(got[i].float()).all()
             assert torch.equal(got[i].view(torch.int16), refs[i].view(torch.int16)), (r, i)
+            q, k, v = ins[i]
+            rows, want = view.expect(q=q, k=k, v=v)
+            assert_close(got[i].cpu()[rows], want, f"replay {r} step {i}")
         _ = (case.q.float() @ case.q.float()[:1].transpose(1, 2).contiguous()).sum()
 
 
@@ -123,6 +133,7 @@ def test_graph_replays_of_the_shared_prefix_pass_match_eager():
     spec = wl.custom("prefix_graph", 32, 8, 128, rows=rows, seed=181, shared_prefix_blocks=pb)
     print(f"\n[case] graph replay shared-prefix pass: S={spec.num_seqs}", flush=True)
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
     q = case.q.clone()
     out = torch.empty_like(q)
@@ -148,4 +159,6 @@ def test_graph_replays_of_the_shared_prefix_pass_match_eager():
         torch.cuda.synchronize()
         assert torch.isfinite(got.float()).all()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        r, want = view.expect(q=q)
+        assert_close(got.cpu()[r], want, f"shared prefix replay {i}")
         _ = (q.float() * 2).sum()

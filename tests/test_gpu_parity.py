@@ -3,10 +3,12 @@
 KV write: bit-exact against oracle.ref_cache_write, and nothing else in the
 pool moves. Attention: max abs error <= 1e-2 and mean abs error <= 1e-3 of
 the kernel's bf16 output against the oracle's float64 result, on every
-named workload (sampled rows at full size) and on a sweep of shapes, edge
-cases and poisoned inputs."""
+named workload (every row of workloads 1, 2, 4 and 5, every decode row and
+one whole chunk of workload 3) and on a sweep of shapes, edge cases and
+poisoned inputs. The oracle's inputs are a CPU copy of what the rows read,
+taken before the library is called (tests/oracle_view.py); the step's new
+tokens enter that copy through the oracle's own ref_cache_write."""
 
-import math
 import random
 
 import pytest
@@ -15,27 +17,15 @@ import torch
 import oracle
 import paged_attention_kv_amd as pa
 import workloads as wl
+from oracle_view import MAX_ABS, MEAN_ABS, OracleView, assert_close, assert_pool_written
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-MAX_ABS = 1e-2
-MEAN_ABS = 1e-3
 
 
 def banner(msg):
     print(f"\n[case] {msg}", flush=True)
-
-
-def assert_close(got, want, what=""):
-    got = got.detach().cpu().double()
-    want = want.detach().cpu().double()
-    assert got.shape == want.shape
-    assert torch.isfinite(got).all(), f"{what}: non-finite output"
-    err = (got - want).abs()
-    mx, mean = err.max().item(), err.mean().item()
-    print(f"  {what}: max abs {mx:.3e} mean abs {mean:.3e} over {got.numel()} values", flush=True)
-    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max {mx:.3e} mean {mean:.3e}"
 
 
 def write_and_forward(case, hints=True, **kw):
@@ -47,38 +37,6 @@ def write_and_forward(case, hints=True, **kw):
                      case.query_start_loc, case.scale, **extra, **kw)
     torch.cuda.synchronize()
     return out
-
-
-def oracle_rows(case, seqs, tokens_per_seq=None):
-    """Oracle output for the listed sequences (optionally only some of their
-    query rows), computed on a CPU copy of just the blocks they read. The
-    step's new tokens are written into that copy by the oracle's own
-    ref_cache_write from the seeded k and v (over whatever the library wrote
-    there), so no oracle input comes from the library.
-    Returns (flattened row indices, [R, Hq, D] float64)."""
-    q, kc, vc, table, lens, qsl, tmap = wl.sequences_subset(case, seqs)
-    bs = case.spec.block_size
-    # the full pool's blocks read by these rows, in the order of the copy
-    bt = case.block_table.cpu()
-    lens_all = case.seq_lens.cpu().tolist()
-    used = torch.unique(torch.cat([bt[sq, :-(-lens_all[sq] // bs)].to(torch.int64)
-                                   for sq in seqs]))
-    slots = case.slot_mapping.cpu()[tmap]
-    keep = slots >= 0
-    blk, off = slots[keep] // bs, slots[keep] % bs
-    pos = torch.searchsorted(used, blk)
-    assert bool((used[pos.clamp(max=len(used) - 1)] == blk).all()), "a new token outside its row"
-    oracle.ref_cache_write(case.k.cpu()[tmap][keep], case.v.cpu()[tmap][keep], pos * bs + off,
-                           kc, vc)
-    pick = None
-    if tokens_per_seq is not None:
-        pick = []
-        for i, s in enumerate(seqs):
-            base = int(qsl[i])
-            pick.extend(base + r for r in tokens_per_seq[s])
-    want = oracle.ref_forward(q, kc, vc, table, lens, qsl, case.scale, tokens=pick)
-    rows = list(range(q.shape[0])) if pick is None else pick
-    return tmap[rows], want[rows]
 
 
 # ---------------------------------------------------------------------------
@@ -93,23 +51,7 @@ def test_cache_write_bit_exact(i):
     k0, v0 = case.k_cache.clone(), case.v_cache.clone()
     pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
     torch.cuda.synchronize()
-    # oracle on a CPU copy of the touched blocks
-    slots = case.slot_mapping.cpu()
-    blocks = torch.unique(slots[slots >= 0] // 16)
-    remap = torch.full((spec.num_blocks,), -1, dtype=torch.int64)
-    remap[blocks] = torch.arange(blocks.numel())
-    local = torch.where(slots >= 0, remap[slots.clamp(min=0) // 16] * 16 + slots.clamp(min=0) % 16,
-                        slots)
-    kc_ref = k0[blocks.to(DEV)].cpu()
-    vc_ref = v0[blocks.to(DEV)].cpu()
-    oracle.ref_cache_write(case.k.cpu(), case.v.cpu(), local, kc_ref, vc_ref)
-    assert torch.equal(case.k_cache[blocks.to(DEV)].cpu().view(torch.int16), kc_ref.view(torch.int16))
-    assert torch.equal(case.v_cache[blocks.to(DEV)].cpu().view(torch.int16), vc_ref.view(torch.int16))
-    # every other block is untouched
-    keep = torch.ones(spec.num_blocks, dtype=torch.bool, device=DEV)
-    keep[blocks.to(DEV)] = False
-    assert torch.equal(case.k_cache[keep].view(torch.int16), k0[keep].view(torch.int16))
-    assert torch.equal(case.v_cache[keep].view(torch.int16), v0[keep].view(torch.int16))
+    assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
 
 
 def test_cache_write_skips_negative_slots():
@@ -135,8 +77,9 @@ def test_tiny_prefill_all_rows(hints):
     spec = wl.config(1)
     banner(f"forward workload 1 (tiny) hints={hints}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, hints=hints)
-    rows, want = oracle_rows(case, list(range(spec.num_seqs)))
+    rows, want = view.expect()
     assert_close(out.cpu()[rows], want, "tiny")
 
 
@@ -145,18 +88,22 @@ def test_decode_workload_all_rows(schedule):
     spec = wl.config(2)
     banner(f"forward workload 2 (decode, 64 rows), schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, decode_schedule=schedule)
-    rows, want = oracle_rows(case, list(range(spec.num_seqs)))
+    rows, want = view.expect()
     assert_close(out.cpu()[rows], want, "decode")
 
 
 def test_decode_workload_fused_write_and_forward_all_rows():
     """Workload 2 as the benchmark times it: one pa_write_and_forward call
     (the write rides in the decode launch) on the default schedule. Every
-    row against the oracle, and the cache rows written bit-exactly."""
+    row against the oracle; the written blocks bit-exact against
+    ref_cache_write and every other block of the pool unchanged."""
     spec = wl.config(2)
     banner("workload 2 through pa_write_and_forward (one launch)")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
     pa.profile_begin()
     out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
                                case.q, case.block_table, case.seq_lens, case.query_start_loc,
@@ -164,49 +111,53 @@ def test_decode_workload_fused_write_and_forward_all_rows():
     torch.cuda.synchronize()
     per = pa.profile_end()
     assert set(per) == {"decode"} and per["decode"][0] == 1, per
-    kc = case.k_cache.view(-1, spec.num_kv_heads, spec.head_size)
-    vc = case.v_cache.view(-1, spec.num_kv_heads, spec.head_size)
-    assert torch.equal(kc[case.slot_mapping].view(torch.int16), case.k.view(torch.int16))
-    assert torch.equal(vc[case.slot_mapping].view(torch.int16), case.v.view(torch.int16))
-    rows, want = oracle_rows(case, list(range(spec.num_seqs)))
+    assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
+    rows, want = view.expect()
     assert_close(out.cpu()[rows], want, "decode, fused write")
 
 
 @pytest.mark.parametrize("schedule", [None, "partitioned"])
-def test_mixed_workload_sampled_rows(schedule):
+def test_mixed_workload_rows(schedule):
+    """The mixed 8192-token step: all 256 decode rows, every query row of
+    the chunk with the longest prior context, and edge and sampled rows of
+    the other three chunks."""
     spec = wl.config(3)
-    banner(f"forward workload 3 (mixed 8192-token step), sampled rows, schedule {schedule}")
+    banner(f"forward workload 3 (mixed 8192-token step), schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
-    out = write_and_forward(case, decode_schedule=schedule).cpu()
-    lens = spec.seq_lens
-    dec = sorted(range(256), key=lambda s: lens[s])
-    dec_pick = sorted(set(dec[:4] + dec[-4:] + random.Random(3).sample(range(256), 12)))
-    rows, want = oracle_rows(case, dec_pick)
-    assert_close(out[rows], want, "mixed/decode rows")
+    chunks = list(range(256, 260))
+    full = max(chunks, key=lambda s: spec.ctx_lens[s])
     edge = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 127, 128, 1023, 1024, 1982, 1983]
-    per = {s: sorted(set(edge + random.Random(s).sample(range(1984), 16))) for s in range(256, 260)}
-    rows, want = oracle_rows(case, list(range(256, 260)), per)
-    assert_close(out[rows], want, "mixed/prefill rows")
+    per = {s: (range(1984) if s == full else
+               sorted(set(edge + random.Random(s).sample(range(1984), 64)))) for s in chunks}
+    dec_view = OracleView(case, range(256))
+    pre_view = OracleView(case, chunks)
+    out = write_and_forward(case, decode_schedule=schedule).cpu()
+    rows, want = dec_view.expect()
+    assert_close(out[rows], want, "mixed/all 256 decode rows")
+    del dec_view
+    rows, want = pre_view.expect(per)
+    assert_close(out[rows], want, f"mixed/prefill rows (chunk {full - 256} whole)")
 
 
 @pytest.mark.parametrize("schedule", [None, "partitioned"])
-def test_long_decode_sampled_rows(schedule):
+def test_long_decode_all_rows(schedule):
     spec = wl.config(4)
-    banner(f"forward workload 4 (16 x 32768 decode), 3 rows, schedule {schedule}")
+    banner(f"forward workload 4 (16 x 32768 decode), all rows, schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, decode_schedule=schedule).cpu()
-    rows, want = oracle_rows(case, [0, 7, 15])
+    rows, want = view.expect()
     assert_close(out[rows], want, "long decode")
 
 
 @pytest.mark.parametrize("shared_flag", [True, False])
-def test_prefix_shared_sampled_rows(shared_flag):
+def test_prefix_shared_all_rows(shared_flag):
     spec = wl.config(5)
-    banner(f"forward workload 5 (prefix-shared decode), 16 rows, shared_blocks={shared_flag}")
+    banner(f"forward workload 5 (prefix-shared decode), all rows, shared_blocks={shared_flag}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, shared_blocks=shared_flag).cpu()
-    pick = sorted(random.Random(5).sample(range(256), 14) + [0, 255])
-    rows, want = oracle_rows(case, pick)
+    rows, want = view.expect()
     assert_close(out[rows], want, "prefix shared")
 
 
@@ -236,13 +187,13 @@ def test_multi_token_decode_rows(name, hq, hkv, d, rows, hinted):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=140 + len(rows))
     banner(f"multi-token decode rows {name}: hinted={hinted} q_lens={spec.q_lens}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     pa.profile_begin()
     out = write_and_forward(case, hints=hinted)
     per = pa.profile_end()
     if hinted:
         assert "prefill" not in per and "plan" not in per, per
-    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
-    r, want = oracle_rows(case, seqs)
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, name)
 
 
@@ -256,9 +207,9 @@ def test_multi_token_decode_rows_schedules(name, hq, hkv, d, rows, schedule):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=140 + len(rows))
     banner(f"multi-token decode rows {name}: schedule {schedule} q_lens={spec.q_lens}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     out = write_and_forward(case, hints=True, decode_schedule=schedule)
-    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
-    r, want = oracle_rows(case, seqs)
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, f"{name} {schedule}")
 
 
@@ -270,8 +221,9 @@ def test_multi_token_decode_rows_on_many_shares():
     rows += [(3, 14), (2, 15), (1, 31)]
     spec = wl.custom("mt_shares", 32, 8, 64, rows=rows, seed=151)
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, hints=True, decode_schedule="even")
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "many shares")
 
 
@@ -282,19 +234,20 @@ def test_multi_token_decode_rows_nan_poison_and_schedules(schedule):
     rows = [(4, 9000), (4, 100), (4, 3), (2, 4000)]
     spec = wl.custom("mt_nan", 32, 8, 128, rows=rows, seed=150)
     case = wl.make_case(spec, device=DEV, poison=float("nan"))
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, hints=True, decode_schedule=schedule)
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, f"nan poison {schedule}")
 
 
 @pytest.mark.parametrize("schedule", [None, "even", "partitioned"])
-def test_spec_decode_workload_sampled_rows(schedule):
+def test_spec_decode_workload_all_rows(schedule):
     spec = wl.spec_decode(4)
     banner(f"speculative-verify workload: 256 rows x 4 query tokens, schedule {schedule}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, decode_schedule=schedule).cpu()
-    pick = sorted(random.Random(16).sample(range(256), 10) + [0, 255])
-    r, want = oracle_rows(case, pick)
+    r, want = view.expect()
     assert_close(out[r], want, "spec decode")
 
 
@@ -311,20 +264,20 @@ def shared_prefix_call(case, prefix_blocks, **kw):
     return out
 
 
-def test_shared_prefix_workload_sampled_rows():
+def test_shared_prefix_workload_all_rows():
     """The prefix-shared decode workload (256 rows, 256 shared blocks + 8 own
-    blocks each): sampled rows against the oracle, and every row close to
-    the per-row decode path."""
+    blocks each): every row against the oracle, and close to the per-row
+    decode path."""
     spec = wl.config(5)
     banner("shared-prefix pass on workload 5 (256 rows, 256-block shared prefix)")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     pa.profile_begin()
     out = shared_prefix_call(case, spec.shared_prefix_blocks).clone()
     per = pa.profile_end()
     # the decode launch merges the prefix chunks' partials itself
     assert per["prefix"][0] == 1 and per["decode"][0] == 1 and "combine" not in per, per
-    pick = sorted(random.Random(15).sample(range(256), 14) + [0, 255])
-    rows, want = oracle_rows(case, pick)
+    rows, want = view.expect()
     assert_close(out.cpu()[rows], want, "shared prefix")
     ref = write_and_forward(case, shared_blocks=True)
     d = (out.float() - ref.float()).abs()
@@ -356,16 +309,14 @@ def test_shared_prefix_cases(name, hq, hkv, d, pb, own):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=120 + pb, shared_prefix_blocks=pb)
     banner(f"shared prefix {name}: S={spec.num_seqs} prefix={pb} blocks Hq={hq} Hkv={hkv} D={d}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = shared_prefix_call(case, pb).clone()
     out2 = pa.forward_shared_prefix(case.q, case.k_cache, case.v_cache, case.block_table,
                                     case.seq_lens, case.query_start_loc, case.scale, pb,
                                     max_seq_len=max(spec.seq_lens))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
-    seqs = list(range(spec.num_seqs))
-    if len(seqs) > 64:
-        seqs = seqs[:24] + seqs[-24:]
-    r, want = oracle_rows(case, seqs)
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, name)
 
 
@@ -409,9 +360,9 @@ def test_sweep_full_oracle(d, hq, hkv):
     spec = wl.custom(f"sweep_d{d}_{hq}x{hkv}", hq, hkv, d, rows=rows, seed=100 + hq + d)
     banner(f"sweep D={d} Hq={hq} Hkv={hkv} rows={rows}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     out = write_and_forward(case, hints=(d == 128))
-    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
-    r, want = oracle_rows(case, seqs)
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, spec.name)
 
 
@@ -421,8 +372,9 @@ def test_long_context_split_into_many_partitions(part):
     spec = wl.custom("longsplit", 32, 4, 64, rows=rows, seed=41)
     banner(f"long rows {rows}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, hints=False)
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "longsplit")
 
 
@@ -455,14 +407,63 @@ def test_decode_schedules(name, hq, hkv, d, rows, schedule):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=60 + len(rows) % 97)
     banner(f"decode schedule {name} ({schedule}): S={spec.num_seqs} Hq={hq} Hkv={hkv} D={d}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     out = write_and_forward(case, decode_schedule=schedule)
     out2 = write_and_forward(case, decode_schedule=schedule).clone()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
-    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
-    if len(seqs) > 64:
-        seqs = seqs[:16] + seqs[len(seqs) // 2 - 8:len(seqs) // 2 + 8] + seqs[-16:]
-    r, want = oracle_rows(case, seqs)
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, name)
+
+
+# ---------------------------------------------------------------------------
+# The separate merge launch of split decode rows
+# ---------------------------------------------------------------------------
+
+# Past 65,536 (row, KV head) pairs the decode kernel has no arrival counter
+# per pair for the in-kernel merge: rows split into several partitions leave
+# partials that decode_combine_kernel merges after the decode launch. Here
+# 4,100 rows x 16 KV heads (65,600 pairs; more rows than the even-share row
+# scan takes, so the partitioned schedule runs), three rows longer than one
+# partition. The short rows see 9..48 keys: a row of two or three keys
+# copies one V value almost whole, and where that value is 4 or more in
+# magnitude a bf16 output is up to 2^-6 from the exact result whatever the
+# kernel does (bf16 steps are 2^-5 there), past the 1e-2 bar (measured
+# with contexts from 0 keys: the largest error, 1.04e-2 on a 2-key row, was
+# the oracle's own result rounded to bf16).
+COMBINE_ROWS = [(1, 8 + (7 * i) % 40) for i in range(4097)] + [(1, 9000), (1, 5000), (1, 3500)]
+
+
+@pytest.mark.parametrize("qmax", [1, 2])
+def test_combine_launch_for_many_rows(qmax):
+    rows = [(2 if (qmax == 2 and i % 3 == 0) else 1, c) for i, (_, c) in enumerate(COMBINE_ROWS)]
+    spec = wl.custom(f"combine_q{qmax}", 32, 16, 64, rows=rows, seed=200 + qmax)
+    banner(f"combine launch: S={spec.num_seqs} Hkv=16 q_len<={qmax}")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    out = write_and_forward(case)
+    per = pa.profile_end()
+    assert per.get("combine", (0,))[0] == 1 and "prefill" not in per, per
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, spec.name)
+
+
+def test_shared_prefix_combine_launch_for_many_rows():
+    """The shared-prefix call past 65,536 (row, KV head) pairs: the prefix
+    chunks' partials and each row's own are merged by the combine launch."""
+    pb = 3
+    rows = [(1, 16 * pb + (1 + (13 * i) % 60) - 1) for i in range(4100)]
+    spec = wl.custom("sp_combine", 32, 16, 64, rows=rows, seed=210, shared_prefix_blocks=pb)
+    banner(f"shared prefix with the combine launch: S={spec.num_seqs} Hkv=16")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    out = shared_prefix_call(case, pb)
+    per = pa.profile_end()
+    assert per["prefix"][0] == 1 and per["decode"][0] == 1, per
+    assert per.get("combine", (0,))[0] == 1, per
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, spec.name)
 
 
 # ---------------------------------------------------------------------------
@@ -500,6 +501,7 @@ def test_write_and_forward_decode_rows(name, hq, hkv, d, rows, schedule):
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=80 + len(rows))
     banner(f"write_and_forward {name} ({schedule}): S={spec.num_seqs} Hq={hq} Hkv={hkv} D={d}")
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     kc_ref, vc_ref = case.k_cache.cpu(), case.v_cache.cpu()
     oracle.ref_cache_write(case.k.cpu(), case.v.cpu(), case.slot_mapping.cpu(), kc_ref, vc_ref)
     pa.profile_begin()
@@ -512,8 +514,7 @@ def test_write_and_forward_decode_rows(name, hq, hkv, d, rows, schedule):
         assert launches["decode"] >= 1, per
     assert torch.equal(case.k_cache.cpu().view(torch.int16), kc_ref.view(torch.int16))
     assert torch.equal(case.v_cache.cpu().view(torch.int16), vc_ref.view(torch.int16))
-    seqs = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0]
-    r, want = oracle_rows(case, seqs)
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, name)
     # the same step as two calls (the cache already holds the new tokens,
     # and rewriting them changes nothing)
@@ -531,6 +532,7 @@ def test_write_and_forward_skips_negative_slots():
     slots[1] = -1
     slots[3] = -7
     case.slot_mapping = slots
+    view = OracleView(case, [0, 2, 4])
     k0, v0 = case.k_cache.clone(), case.v_cache.clone()
     out = fused_call(case, "partitioned").clone()
     kc, vc = case.k_cache.clone(), case.v_cache.clone()
@@ -540,7 +542,7 @@ def test_write_and_forward_skips_negative_slots():
     assert torch.equal(kc.view(torch.int16), case.k_cache.view(torch.int16))
     assert torch.equal(vc.view(torch.int16), case.v_cache.view(torch.int16))
     assert torch.equal(out.view(torch.int16), two.view(torch.int16))
-    r, want = oracle_rows(case, [0, 2, 4])
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "rows with slots")
 
 
@@ -548,11 +550,12 @@ def test_write_and_forward_mixed_batch_falls_back_to_two_launches():
     rows = [(1, 900), (37, 100), (1, 33), (200, 200), (1, 5000)]
     spec = wl.custom("mixed_fused", 32, 8, 128, rows=rows, seed=92)
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     pa.profile_begin()
     out = fused_call(case, max_query_len=200)
     per = pa.profile_end()
     assert per["cache_write"][0] == 1 and per["prefill"][0] == 1 and per["decode"][0] == 1
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "mixed")
 
 
@@ -561,8 +564,9 @@ def test_nan_poison_outside_context_does_not_leak():
     spec = wl.custom("nanpoison", 32, 8, 128, rows=rows, seed=42)
     banner("NaN-poisoned pool")
     case = wl.make_case(spec, device=DEV, poison=float("nan"))
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case)
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "nan poison")
 
 
@@ -571,8 +575,9 @@ def test_table_padding_poisoned_with_int32_max():
     spec = wl.custom("padmax", 16, 2, 64, rows=rows, seed=43, max_blocks_per_seq=40)
     case = wl.make_case(spec, device=DEV, table_pad=2**31 - 1)
     banner("table padding = INT32_MAX")
+    view = OracleView(case, range(spec.num_seqs))
     out = write_and_forward(case, hints=False)
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "int32max padding")
 
 
@@ -588,8 +593,9 @@ def test_row_order_does_not_matter_and_runs_are_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)), "not deterministic"
     b = wl.make_case(rev, device=DEV)
+    view = OracleView(b, range(rev.num_seqs))
     outb = write_and_forward(b)
-    r, want = oracle_rows(b, list(range(rev.num_seqs)))
+    r, want = view.expect()
     assert_close(outb.cpu()[r], want, "reversed rows")
 
 
@@ -601,9 +607,10 @@ def test_chunked_prefill_matches_one_shot():
     spec = wl.custom("oneshot", Hq, Hkv, D, rows=[(P, c)], seed=45, num_blocks=64)
     case = wl.make_case(spec, device=DEV)
     banner("chunked prefill 8+8+2 vs one shot")
+    view = OracleView(case, [0])
     kc0, vc0 = case.k_cache.clone(), case.v_cache.clone()
     one = write_and_forward(case)
-    r, want = oracle_rows(case, [0])
+    r, want = view.expect()
     assert_close(one.cpu()[r], want, "one shot")
     kc, vc = kc0, vc0
     outs = []
@@ -662,9 +669,9 @@ def test_workspace_shared_by_calls_of_different_shapes():
     for spec in (few, many, few, many, few):
         banner(f"workspace reuse: {spec.name}")
         case = wl.make_case(spec, device=DEV)
+        view = OracleView(case, range(spec.num_seqs))
         out = write_and_forward(case, workspace=ws)
-        pick = list(range(0, spec.num_seqs, max(1, spec.num_seqs // 6)))
-        r, want = oracle_rows(case, pick)
+        r, want = view.expect()
         assert_close(out.cpu()[r], want, spec.name)
         assert int(ws[:pa.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, "counters left nonzero"
 
@@ -672,6 +679,7 @@ def test_workspace_shared_by_calls_of_different_shapes():
 def test_kernel_timing_records_each_launch_class():
     spec = wl.custom("prof", 32, 8, 128, rows=[(1, 3000), (40, 100), (1, 20)], seed=49)
     case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
     pa.profile_begin()
     out = write_and_forward(case)
     per = pa.profile_end()
@@ -679,7 +687,7 @@ def test_kernel_timing_records_each_launch_class():
     assert per["plan"][0] == 1 and per["prefill_short"][0] == 1
     assert all(ms > 0 for _, ms in per.values())
     # timing does not change results
-    r, want = oracle_rows(case, list(range(spec.num_seqs)))
+    r, want = view.expect()
     assert_close(out.cpu()[r], want, "profiled forward")
 
 
