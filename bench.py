@@ -7,21 +7,30 @@ partitioned schedule; a write launch and the forward launches otherwise).
 Inputs are synthetic, seeded, and resident in HBM before the timed region
 starts.
 
-Headline (one JSON line on stdout):
+One JSON line on stdout:
   * value: decode GB/s on the decode workload (64 sequences x 1 query token,
     context U[512, 2048], 32 q / 4 kv heads, D 64, 16-token blocks, 100k-block
     bf16 pool); bytes are algorithmic (each row's K and V context once, q, out,
     and the KV write), time is the whole step. Eight disjoint block-table sets
     drawn from the same pool rotate between steps so the 256 MiB Infinity
-    Cache cannot hold a step's KV.
-  * mixed_step: tokens/s of the 8192-token mixed chunked-prefill step (256
-    decode rows + 4 x 1984-token chunks, 32 q / 8 kv heads, D 128).
+    Cache cannot hold a step's KV. config.step_us gives the median, p10 and
+    p90 of single steps; config.graph_* the same step replayed from graphs.
   * roofline: the decode kernel's algorithmic bytes per launch (with the
     KV write when the launch does it) over its average launch duration (HIP
-    events on the launch stream), against 8 TB/s.
-  * cpu_baseline: the CPU oracle timed on this host on a bounded sample.
+    events on the launch stream), against 8 TB/s, with the read probe.
+  * mixed_step: tokens/s of the 8192-token mixed chunked-prefill step (256
+    decode rows + 4 x 1984-token chunks, 32 q / 8 kv heads, D 128), and its
+    decode rows (HBM roofline) and prefill rows (bf16 matrix-core roofline)
+    timed apart.
+  * workloads: the other named workloads, each with its roofline fraction:
+    long_decode (16 x 32768), prefix_shared (256 rows sharing a 4096-token
+    prefix, per-row path and shared-prefix pass), tiny (two short prompts)
+    and spec_verify (256 rows of 4 query tokens).
+  * cpu_baseline: the CPU oracle (float32) timed on this host on one step of
+    the decode workload, all threads and one thread.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only decode|mixed]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+                       [--only decode|mixed|long|prefix|tiny|spec_decode|...]
 """
 
 from __future__ import annotations
@@ -46,6 +55,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATIONS = 8
 COPY_MIB = 512
+GRAPH_NOTE = ("the same step captured in a HIP graph per block-table set and replayed "
+              "(value uses eager launches)")
 
 
 # ---------------------------------------------------------------------------
@@ -139,14 +150,27 @@ class StepInputs:
 FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan", "prefix")
 
 
+def percentile(xs, f):
+    """The f-quantile (0..1) of xs by linear interpolation between ranks."""
+    v = sorted(xs)
+    if not v:
+        return float("nan")
+    x = f * (len(v) - 1)
+    lo = int(math.floor(x))
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (x - lo)
+
+
 def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool = False):
     """Time `steps` steps (KV write + forward). Pass 1 is bracketed by
     synchronize and timed with HIP events on the launch stream, with nothing
-    else inside (the step time). Pass 2 repeats the steps with the library's
-    kernel timing on (pa.profile_begin/end: HIP events around every kernel
-    launch on its stream). Returns (ms per step, {kernel class: mean ms per
-    launch}, {kernel class: launches per step}, ms of forward kernels per
-    step)."""
+    else inside: the step time. Pass 2 records an event between consecutive
+    steps for the distribution of single steps (median, p10, p90; the events
+    add their own packets, so these read a little longer). Pass 3 repeats
+    the steps with the library's kernel timing on (pa.profile_begin/end: HIP
+    events around every kernel launch on its stream). Returns a dict:
+    ms_step, ms_median, ms_p10, ms_p90, kernels {class: mean ms per launch},
+    counts {class: launches per step}, ms_fwd (forward kernels per step)."""
     spec = inp.spec
 
     def step(i):
@@ -173,14 +197,29 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool 
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i].record()
+        step(i)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    each = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     pa.profile_begin()
     for i in range(steps):
         step(i)
     per = pa.profile_end()
-    mean = {k: v[1] / v[0] for k, v in per.items()}
-    count = {k: v[0] / steps for k, v in per.items()}
-    ms_fwd = sum(per[k][1] for k in FORWARD_KERNELS if k in per) / steps
-    return ms_step, mean, count, ms_fwd
+    return dict(ms_step=ms_step, ms_median=percentile(each, 0.5), ms_p10=percentile(each, 0.1),
+                ms_p90=percentile(each, 0.9),
+                kernels={k: v[1] / v[0] for k, v in per.items()},
+                counts={k: v[0] / steps for k, v in per.items()},
+                ms_fwd=sum(per[k][1] for k in FORWARD_KERNELS if k in per) / steps)
+
+
+def dist_us(t):
+    """Step-time distribution of a run_steps result, in microseconds."""
+    return {"median": round(t["ms_median"] * 1e3, 3), "p10": round(t["ms_p10"] * 1e3, 3),
+            "p90": round(t["ms_p90"] * 1e3, 3)}
 
 
 def run_graph_steps(pa, inp: StepInputs, steps: int, warmup: int) -> float:
@@ -330,31 +369,301 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
-def cpu_baseline(spec, budget_s: float = 12.0):
-    """Time the oracle (float64, as it stands) on all rows of the workload
-    for about budget_s seconds of CPU work on this host."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(spec, budget_s: float = 6.0):
+    """The oracle as it stands, in float32, on this host: one step of the
+    workload (the KV write of its new tokens with ref_cache_write, then
+    ref_forward over all rows) on a CPU copy of just the blocks the rows
+    read. Timed with all of torch's threads and with one thread: one warm-up
+    run, then runs until at least 3 and about budget_s seconds; the median
+    run counts. Input generation and the copy are outside the timing."""
     import oracle
     case = wl.make_case(spec, device="cpu")
-    q, kc, vc, table, lens, qsl, _ = wl.sequences_subset(case, list(range(spec.num_seqs)))
-    k, v, slots = case.k, case.v, case.slot_mapping
-    # the write touches the compacted pool: remap slots into it
-    n = 0
-    t_start = time.perf_counter()
-    while True:
-        kc2, vc2 = kc.clone(), vc.clone()
-        oracle.ref_cache_write(k[:0], v[:0], slots[:0], kc2, vc2)
-        oracle.ref_forward(q, kc2, vc2, table, lens, qsl, spec.scale)
-        n += 1
-        el = time.perf_counter() - t_start
-        if el >= budget_s or n >= 1000:
-            break
-    per = el / n
-    gbs = (attention_bytes(spec) + write_bytes(spec)) / per / 1e9
-    return dict(value=round(gbs, 4), unit="GB/s", cores=torch.get_num_threads(), kind="oracle",
-                sample=(f"all {spec.num_seqs} rows of the decode workload, oracle ref_forward in "
-                        f"float64 (PyTorch CPU), {n} repetitions in {el:.1f} s "
-                        f"({per * 1e3:.1f} ms per step)"),
-                ms_per_step=round(per * 1e3, 3))
+    q, kc, vc, table, lens, qsl, tmap = wl.sequences_subset(case, list(range(spec.num_seqs)))
+    # the new tokens' slots in the compacted copy of the pool (plumbing: the
+    # same block and row, renumbered the way sequences_subset renumbers)
+    bs = spec.block_size
+    bt = case.block_table
+    used = torch.unique(torch.cat([bt[s_, :-(-L // bs)].to(torch.int64)
+                                   for s_, L in enumerate(spec.seq_lens)]))
+    slots = case.slot_mapping[tmap]
+    local = torch.searchsorted(used, slots // bs) * bs + slots % bs
+    k, v = case.k[tmap], case.v[tmap]
+    nbytes = attention_bytes(spec) + write_bytes(spec)
+
+    def one_step():
+        oracle.ref_cache_write(k, v, local, kc, vc)
+        oracle.ref_forward(q, kc, vc, table, lens, qsl, spec.scale, dtype=torch.float32)
+
+    default_threads = torch.get_num_threads()
+    runs = {}
+    for threads in (default_threads, 1):
+        torch.set_num_threads(threads)
+        one_step()
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < 3 or (time.perf_counter() - t_start < budget_s and len(times) < 200):
+            t = time.perf_counter()
+            one_step()
+            times.append(time.perf_counter() - t)
+        med = percentile(times, 0.5)
+        runs[threads] = dict(ms_per_step=round(med * 1e3, 3), runs=len(times),
+                             gbs=round(nbytes / med / 1e9, 4))
+    torch.set_num_threads(default_threads)
+    full, one = runs[default_threads], runs[1]
+    return dict(value=full["gbs"], unit="GB/s", cores=default_threads, kind="oracle",
+                sample=(f"one step of the decode workload: ref_cache_write of its {spec.num_tokens} "
+                        f"new tokens and ref_forward of all {spec.num_seqs} rows in float32 "
+                        f"(PyTorch CPU) on a copy of the blocks they read; median of "
+                        f"{full['runs']} runs after a warm-up"),
+                ms_per_step=full["ms_per_step"], cpu_model=cpu_model(),
+                nproc=os.cpu_count(),
+                one_thread={"value": one["gbs"], "ms_per_step": one["ms_per_step"],
+                            "runs": one["runs"]})
+
+
+# ---------------------------------------------------------------------------
+# Workload legs
+# ---------------------------------------------------------------------------
+
+def progress(msg):
+    """One line on stderr as each part of the run ends (stdout holds only the
+    JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def frac(x, peak):
+    return round(x / peak, 4)
+
+
+def leg_decode(pa, args, dev):
+    """Workload 2, the headline: the decode step through one
+    pa_write_and_forward launch, graph replays, and the read probe."""
+    spec = wl.config(2)
+    inp = StepInputs(spec, ROTATIONS, dev)
+    t = run_steps(pa, inp, args.steps, args.warmup)
+    b_attn = attention_bytes(spec)
+    b_step = b_attn + write_bytes(spec)
+    gbs = b_step / (t["ms_step"] * 1e-3) / 1e9
+    ms_graph = run_graph_steps(pa, inp, args.steps, args.warmup)
+    ms_graph_loop = run_graph_loop(pa, inp, args.steps, args.warmup)
+    ms_probe, probe_shape, probe_bytes = run_read_probe(pa, inp, args.steps, args.warmup)
+    kcount = t["counts"]
+    fused = "cache_write" not in kcount  # the decode launch also wrote the new tokens
+    one_launch = set(kcount) == {"decode"} and abs(kcount["decode"] - 1.0) < 1e-9
+    # A step that is one launch: its duration is the events around the
+    # whole timed region over the launches in it (gaps between launches
+    # included, so never shorter than the kernel). Events around each
+    # launch add their own packets to it and read longer.
+    ms_dec = t["ms_step"] if one_launch else t["kernels"]["decode"]
+    b_dec = b_step if fused else b_attn
+    kernel_gbs = b_dec / (ms_dec * 1e-3) / 1e9
+    config = {
+        "workload": ("decode step: 64 sequences x 1 query token, context U[512,2048], "
+                     "32 q / 4 kv heads, head_size 64, block 16, 100k-block bf16 pool; "
+                     "KV write + paged attention"),
+        "tokens": spec.num_tokens, "kv_bytes_per_step": b_step,
+        "step_us": dist_us(t),
+        "graph_replay": {"ms_per_step": round(ms_graph, 5),
+                         "gbs": round(b_step / (ms_graph * 1e-3) / 1e9, 2),
+                         "note": GRAPH_NOTE},
+        "graph_of_rotations": {"ms_per_step": round(ms_graph_loop, 5),
+                               "gbs": round(b_step / (ms_graph_loop * 1e-3) / 1e9, 2),
+                               "steps_per_graph": inp.rotations,
+                               "note": "one graph holding one step per block-table set, "
+                                       "replayed whole"},
+        "block_table_rotations": inp.rotations,
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+    kname = "decode_kernel<64, 2, true, %s, false>" % ("true" if fused else "false")
+    pgbs = probe_bytes / (ms_probe * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": round(kernel_gbs, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": frac(kernel_gbs, HBM_PEAK_GBS),
+                "traffic": measured_traffic(kname, "decode ("),
+                "avg_launch_us": round(ms_dec * 1e3, 3),
+                "avg_launch_us_from": ("events around the timed region / launches"
+                                       if one_launch else "events around each launch"),
+                "algorithmic_bytes_per_launch": b_dec,
+                "forward_kernels_us_per_step": round(t["ms_fwd"] * 1e3, 3),
+                "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+                "read_probe": {
+                    "what": "the same blocks read whole with no arithmetic "
+                            "(pa_probe_block_read), best of %d launch shapes" % len(PROBE_SHAPES),
+                    "us": round(ms_probe * 1e3, 3), "bytes": probe_bytes, "gbs": round(pgbs, 1),
+                    "frac_of_peak": frac(pgbs, HBM_PEAK_GBS),
+                    "waves_blocks_per_wg": list(probe_shape),
+                    "kernel_frac_of_probe": round(kernel_gbs / pgbs, 4)}}
+    return dict(value=round(gbs, 2), ms_step=t["ms_step"], config=config, roofline=roofline)
+
+
+def leg_mixed(pa, args, dev):
+    """Workload 3: the mixed chunked-prefill step (tokens/s), and its decode
+    and prefill rows timed as batches of their own to attribute HBM and
+    matrix-core use."""
+    spec = wl.config(3)
+    inp = StepInputs(spec, 1, dev)
+    t = run_steps(pa, inp, args.steps, args.warmup)
+    dec_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] == 1]
+    pre_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 1]
+    del inp
+    torch.cuda.empty_cache()
+    sub = {}
+    for name, rows in (("decode_rows", dec_rows), ("prefill_rows", pre_rows)):
+        ss = sub_spec(spec, rows, name)
+        si = StepInputs(ss, 1, dev)
+        st = run_steps(pa, si, args.steps, args.warmup)
+        sub[name] = dict(t=st, bytes=attention_bytes(ss), flops=attention_flops(ss))
+        del si
+        torch.cuda.empty_cache()
+    pre, dec = sub["prefill_rows"], sub["decode_rows"]
+    pre_ms, dec_ms = pre["t"]["ms_fwd"], dec["t"]["ms_fwd"]
+    pre_tf = pre["flops"] / (pre_ms * 1e-3) / 1e12
+    tile_us = pre["t"]["kernels"].get("prefill", float("nan")) * 1e3
+    dec_gbs = dec["bytes"] / (dec_ms * 1e-3) / 1e9
+    return {
+        "workload": ("mixed chunked-prefill step, 8192 new tokens: 256 decode rows (context "
+                     "U[256,8192]) + 4 chunks of 1984 tokens (prior context U[0,4096]); "
+                     "32 q / 8 kv heads, head_size 128"),
+        "tokens_per_s": round(spec.num_tokens / (t["ms_step"] * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(t["ms_step"], 4), "step_us": dist_us(t),
+        "ms_forward_kernels": round(t["ms_fwd"], 4),
+        "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+        "prefill_rows": {
+            "ms": round(pre_ms, 4), "flops": pre["flops"],
+            "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in pre["t"]["kernels"].items()},
+            "tflops": round(pre_tf, 2),
+            "roofline": {"bound": "mfma", "kernel": "prefill_tile_kernel (all forward launches)",
+                         "achieved": round(pre_tf, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": frac(pre_tf, BF16_PEAK_TFLOPS)},
+            "tile_kernel_frac_of_bf16_peak": frac(pre["flops"] / (tile_us * 1e-6) / 1e12,
+                                                  BF16_PEAK_TFLOPS)},
+        "decode_rows": {
+            "ms": round(dec_ms, 4), "bytes": dec["bytes"],
+            "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in dec["t"]["kernels"].items()},
+            "gbs": round(dec_gbs, 2),
+            "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel<128, 2, true>",
+                         "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": frac(dec_gbs, HBM_PEAK_GBS)}}}
+
+
+def leg_long(pa, args, dev):
+    """Workload 4: 16 rows at context 32768, the rows shared out evenly."""
+    spec = wl.config(4)
+    inp = StepInputs(spec, 1, dev)
+    t = run_steps(pa, inp, args.steps, args.warmup)
+    b = attention_bytes(spec)
+    gbs = b / (t["ms_fwd"] * 1e-3) / 1e9
+    pms, pshape, pbytes = run_read_probe(pa, inp, args.steps, args.warmup)
+    pgbs = pbytes / (pms * 1e-3) / 1e9
+    return {
+        "workload": spec.description, "ms_per_step": round(t["ms_step"], 5),
+        "step_us": dist_us(t), "ms_forward_kernels": round(t["ms_fwd"], 5),
+        "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+        "tokens_per_s": round(spec.num_tokens / (t["ms_step"] * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel<128, 2, true>",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": frac(gbs, HBM_PEAK_GBS), "algorithmic_bytes_per_launch": b,
+                     "kernel_trace": "profiles/decode_stream_kernel_long-decode-16x32768.md"},
+        "read_probe": {"us": round(pms * 1e3, 3), "gbs": round(pgbs, 1),
+                       "frac_of_peak": frac(pgbs, HBM_PEAK_GBS),
+                       "waves_blocks_per_wg": list(pshape),
+                       "forward_frac_of_probe": round(gbs / pgbs, 4)}}
+
+
+def leg_prefix(pa, args, dev):
+    """Workload 5: 256 rows sharing a 4096-token prefix, on the per-row path
+    and through the shared-prefix pass."""
+    spec = wl.config(5)
+    inp = StepInputs(spec, ROTATIONS, dev)
+    b = attention_bytes(spec)
+    blk = 2 * spec.block_size * spec.num_kv_heads * spec.head_size * 2
+    uniq = (spec.shared_prefix_blocks + spec.num_seqs * (
+        spec.max_blocks_per_seq - spec.shared_prefix_blocks)) * blk
+    pre_flops = (4 * spec.head_size * spec.num_q_heads * spec.num_seqs
+                 * spec.shared_prefix_blocks * spec.block_size)
+    out = {"workload": spec.description, "rotations": inp.rotations,
+           "logical_bytes": b, "unique_bytes": uniq}
+    for name, sp in (("per_row_path", False), ("shared_prefix_pass", True)):
+        t = run_steps(pa, inp, args.steps, args.warmup, shared_prefix=sp)
+        e = {"ms_per_step": round(t["ms_step"], 5), "step_us": dist_us(t),
+             "ms_forward_kernels": round(t["ms_fwd"], 5),
+             "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+             "forward_gbs_logical": round(b / (t["ms_fwd"] * 1e-3) / 1e9, 2),
+             "forward_gbs_unique": round(uniq / (t["ms_fwd"] * 1e-3) / 1e9, 2),
+             "tokens_per_s": round(spec.num_tokens / (t["ms_step"] * 1e-3), 1)}
+        e["roofline"] = {"bound": "hbm", "achieved": e["forward_gbs_unique"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": frac(e["forward_gbs_unique"], HBM_PEAK_GBS),
+                         "bytes": "unique (each shared block counted once)"}
+        if sp and "prefix" in t["kernels"]:
+            tf = pre_flops / (t["kernels"]["prefix"] * 1e-3) / 1e12
+            e["prefix_kernel"] = {"bound": "mfma", "achieved": round(tf, 2),
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": frac(tf, BF16_PEAK_TFLOPS), "flops": pre_flops}
+        out[name] = e
+    return out
+
+
+def leg_tiny(pa, args, dev):
+    """Workload 1: two short prompts (launch-bound; parity is its point)."""
+    spec = wl.config(1)
+    inp = StepInputs(spec, 1, dev)
+    t = run_steps(pa, inp, args.steps, args.warmup)
+    ms_graph = run_graph_steps(pa, inp, args.steps, args.warmup)
+    return {"workload": spec.description, "ms_per_step": round(t["ms_step"], 5),
+            "step_us": dist_us(t), "ms_forward_kernels": round(t["ms_fwd"], 5),
+            "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+            "launches_per_step": {k: round(v, 2) for k, v in t["counts"].items()},
+            "bound": "launch", "flops": attention_flops(spec),
+            "graph_replay": {"ms_per_step": round(ms_graph, 5),
+                             "note": "the step's launches captured in one HIP graph and "
+                                     "replayed (ms_per_step uses eager launches)"}}
+
+
+def leg_spec(pa, args, dev):
+    """Rows verifying 3 drafted tokens (4 query tokens each): on the decode
+    path (the tight max_query_len hint) and on the prefill path."""
+    spec = wl.spec_decode(4)
+    inp = StepInputs(spec, 1, dev)
+    b = attention_bytes(spec)
+    t = run_steps(pa, inp, args.steps, args.warmup)
+    gbs = b / (t["ms_fwd"] * 1e-3) / 1e9
+    out = {"workload": spec.description, "ms_per_step": round(t["ms_step"], 5),
+           "step_us": dist_us(t), "ms_forward_kernels": round(t["ms_fwd"], 5),
+           "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+           "forward_gbs_logical": round(gbs, 2),
+           "roofline": {"bound": "hbm", "kernel": "decode_stream_kernel<128, 2, true>",
+                        "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": frac(gbs, HBM_PEAK_GBS)}}
+    inp.hints["max_query_len"] = None
+    t2 = run_steps(pa, inp, args.steps, args.warmup)
+    out["prefill_path"] = {
+        "ms_per_step": round(t2["ms_step"], 5), "ms_forward_kernels": round(t2["ms_fwd"], 5),
+        "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t2["kernels"].items()},
+        "forward_gbs_logical": round(b / (t2["ms_fwd"] * 1e-3) / 1e9, 2)}
+    return out
+
+
+def leg_sub(pa, args, dev, which):
+    """Workload 3's decode rows or prefill rows alone (profiling runs)."""
+    m3 = wl.config(3)
+    rows = [s for s in range(m3.num_seqs) if (m3.q_lens[s] == 1) == (which == "mixed_decode")]
+    spec = sub_spec(m3, rows, which)
+    inp = StepInputs(spec, 1, dev)
+    t = run_steps(pa, inp, args.steps, args.warmup)
+    return {"workload": which, "ms_per_step": round(t["ms_step"], 5),
+            "ms_forward_kernels": round(t["ms_fwd"], 5),
+            "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()}}
 
 
 # ---------------------------------------------------------------------------
@@ -369,7 +678,7 @@ def main(argv=None):
                                        "mixed_decode", "mixed_prefill", "spec_decode"],
                     default=None)
     ap.add_argument("--all", action="store_true",
-                    help="also time the long-decode, prefix-shared and tiny workloads")
+                    help="accepted for compatibility: every workload runs by default")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -381,7 +690,6 @@ def main(argv=None):
     import paged_attention_kv_amd as pa
     pa.load_library()
     dev = "cuda:0"
-    result = {}
     if args.only == "copy":
         # Calibration for the HBM byte counters: a plain device-to-device copy
         # of a known size (COPY_MIB read + COPY_MIB written per launch).
@@ -394,193 +702,49 @@ def main(argv=None):
         print(json.dumps({"copy_mib": COPY_MIB, "launches": args.warmup + args.steps}), flush=True)
         return 0
 
-    if args.only in (None, "decode"):
-        spec = wl.config(2)
-        inp = StepInputs(spec, ROTATIONS, dev)
-        ms_step, kmean, kcount, ms_fwd = run_steps(pa, inp, args.steps, args.warmup)
-        b_attn = attention_bytes(spec)
-        b_step = b_attn + write_bytes(spec)
-        gbs = b_step / (ms_step * 1e-3) / 1e9
-        ms_graph = run_graph_steps(pa, inp, args.steps, args.warmup)
-        ms_graph_loop = run_graph_loop(pa, inp, args.steps, args.warmup)
-        ms_probe, probe_shape, probe_bytes = run_read_probe(pa, inp, args.steps, args.warmup)
-        fused = "cache_write" not in kcount  # the decode launch also wrote the new tokens
-        one_launch = set(kcount) == {"decode"} and abs(kcount["decode"] - 1.0) < 1e-9
-        # A step that is one launch: its duration is the events around the
-        # whole timed region over the launches in it (gaps between launches
-        # included, so never shorter than the kernel). Events around each
-        # launch add their own packets to it and read longer.
-        ms_dec = ms_step if one_launch else kmean["decode"]
-        b_dec = b_step if fused else b_attn
-        result["decode"] = dict(ms_step=ms_step, gbs=gbs, ms_fwd=ms_fwd, ms_decode_kernel=ms_dec,
-                                kernel_gbs=b_dec / (ms_dec * 1e-3) / 1e9, bytes_step=b_step,
-                                bytes_fwd=b_dec, fused=fused, rotations=inp.rotations,
-                                ms_graph=ms_graph, ms_graph_loop=ms_graph_loop,
-                                one_launch=one_launch,
-                                probe=(ms_probe, probe_shape, probe_bytes),
-                                kernels={k: round(v * 1e3, 3) for k, v in kmean.items()})
-        del inp
-        torch.cuda.empty_cache()
-
-    if args.only in (None, "mixed"):
-        spec = wl.config(3)
-        inp = StepInputs(spec, 1, dev)
-        ms_step, kmean_m, _, ms_fwd = run_steps(pa, inp, max(5, args.steps // 5),
-                                                max(2, args.warmup // 2))
-        dec_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] == 1]
-        pre_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 1]
-        del inp
-        torch.cuda.empty_cache()
-        sub = {}
-        for name, rows in (("decode_rows", dec_rows), ("prefill_rows", pre_rows)):
-            ss = sub_spec(spec, rows, name)
-            si = StepInputs(ss, 1, dev)
-            _, km, _, f_ms = run_steps(pa, si, max(5, args.steps // 5), 2)
-            sub[name] = dict(ms_fwd=f_ms, bytes=attention_bytes(ss), flops=attention_flops(ss),
-                             kernels={k: round(v * 1e3, 3) for k, v in km.items()})
-            del si
-            torch.cuda.empty_cache()
-        tok_s = spec.num_tokens / (ms_step * 1e-3)
-        result["mixed"] = dict(ms_step=ms_step, tokens_per_s=tok_s, ms_fwd=ms_fwd, sub=sub,
-                               kernels={k: round(v * 1e3, 3) for k, v in kmean_m.items()})
-
-    others = []
-    if args.all or args.only in ("long", "prefix", "tiny", "mixed_decode", "mixed_prefill",
-                                 "spec_decode"):
-        m3 = wl.config(3)
-        for name, i, rot in (("long", 4, 1), ("prefix", 5, ROTATIONS), ("tiny", 1, 1),
-                             ("spec_decode", 6, 1), ("mixed_decode", 3, 1),
-                             ("mixed_prefill", 3, 1)):
-            if args.only != name and (args.only is not None or name.startswith("mixed_")):
-                continue
-            spec = wl.spec_decode(4) if name == "spec_decode" else wl.config(i)
-            if name == "mixed_decode":
-                spec = sub_spec(m3, [s for s in range(m3.num_seqs) if m3.q_lens[s] == 1], name)
-            if name == "mixed_prefill":
-                spec = sub_spec(m3, [s for s in range(m3.num_seqs) if m3.q_lens[s] > 1], name)
-            inp = StepInputs(spec, rot, dev)
-            ms_step, km, _, ms_fwd = run_steps(pa, inp, args.steps, args.warmup)
-            b = attention_bytes(spec)
-            entry = dict(workload=spec.description or spec.name, ms_per_step=round(ms_step, 5),
-                         ms_forward_kernels=round(ms_fwd, 5), rotations=inp.rotations,
-                         forward_gbs_logical=round(b / (ms_fwd * 1e-3) / 1e9, 2),
-                         kernel_avg_us={k: round(v * 1e3, 3) for k, v in km.items()},
-                         tokens_per_s=round(spec.num_tokens / (ms_step * 1e-3), 1))
-            if i == 5:
-                uniq = (spec.shared_prefix_blocks + spec.num_seqs * (
-                    spec.max_blocks_per_seq - spec.shared_prefix_blocks)) * \
-                    2 * spec.block_size * spec.num_kv_heads * spec.head_size * 2
-                entry["forward_gbs_unique"] = round(uniq / (ms_fwd * 1e-3) / 1e9, 2)
-                # the same step through pa_forward_shared_prefix
-                ms2, km2, _, fwd2 = run_steps(pa, inp, args.steps, args.warmup, shared_prefix=True)
-                entry["shared_prefix_pass"] = {
-                    "ms_per_step": round(ms2, 5), "ms_forward_kernels": round(fwd2, 5),
-                    "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in km2.items()},
-                    "forward_gbs_logical": round(b / (fwd2 * 1e-3) / 1e9, 2),
-                    "forward_gbs_unique": round(uniq / (fwd2 * 1e-3) / 1e9, 2),
-                    "tokens_per_s": round(spec.num_tokens / (ms2 * 1e-3), 1)}
-            if i == 4:
-                entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-                pms, pshape, pbytes = run_read_probe(pa, inp, max(5, args.steps // 5), 2)
-                pgbs = pbytes / (pms * 1e-3) / 1e9
-                entry["read_probe"] = {"us": round(pms * 1e3, 3), "gbs": round(pgbs, 1),
-                                       "waves_blocks_per_wg": list(pshape),
-                                       "forward_frac_of_probe": round(b / (ms_fwd * 1e-3) / 1e9
-                                                                      / pgbs, 4)}
-            if name == "spec_decode":
-                entry["frac_of_hbm_peak"] = round(b / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-                # the same rows without the tight hint: the prefill path
-                inp.hints["max_query_len"] = None
-                ms2, km2, _, fwd2 = run_steps(pa, inp, args.steps, args.warmup)
-                entry["prefill_path"] = {
-                    "ms_per_step": round(ms2, 5), "ms_forward_kernels": round(fwd2, 5),
-                    "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in km2.items()},
-                    "forward_gbs_logical": round(b / (fwd2 * 1e-3) / 1e9, 2)}
-            others.append((name, entry))
-            del inp
-            torch.cuda.empty_cache()
-
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) bf16 values, seeded lengths and block placement)"}
-    if "decode" in result:
-        d = result["decode"]
-        line.update(value=round(d["gbs"], 2), unit="GB/s", ms_per_step=round(d["ms_step"], 5))
-        line["config"] = {
-            "workload": ("decode step: 64 sequences x 1 query token, context U[512,2048], "
-                         "32 q / 4 kv heads, head_size 64, block 16, 100k-block bf16 pool; "
-                         "KV write + paged attention"),
-            "tokens": 64, "kv_bytes_per_step": d["bytes_step"],
-            "graph_replay": {"ms_per_step": round(d["ms_graph"], 5),
-                             "gbs": round(d["bytes_step"] / (d["ms_graph"] * 1e-3) / 1e9, 2),
-                             "note": "the same step captured in a HIP graph per block-table "
-                                     "set and replayed (value uses eager launches)"},
-            "graph_of_rotations": {"ms_per_step": round(d["ms_graph_loop"], 5),
-                                   "gbs": round(d["bytes_step"] / (d["ms_graph_loop"] * 1e-3) / 1e9,
-                                                2),
-                                   "steps_per_graph": d["rotations"],
-                                   "note": "one graph holding one step per block-table set, "
-                                           "replayed whole"},
-            "block_table_rotations": d["rotations"],
-            "pct_of_hbm_peak": round(100 * d["gbs"] / HBM_PEAK_GBS, 2)}
-        kname = "decode_kernel<64, 2, true, %s, false>" % ("true" if d["fused"] else "false")
-        line["roofline"] = {"bound": "hbm", "kernel": kname,
-                            "achieved": round(d["kernel_gbs"], 2), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(d["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic(kname, "decode ("),
-                            "avg_launch_us": round(d["ms_decode_kernel"] * 1e3, 3),
-                            "avg_launch_us_from": ("events around the timed region / launches"
-                                                   if d["one_launch"] else
-                                                   "events around each launch"),
-                            "algorithmic_bytes_per_launch": d["bytes_fwd"],
-                            "forward_kernels_us_per_step": round(d["ms_fwd"] * 1e3, 3),
-                            "kernel_avg_us": d["kernels"]}
-        pms, pshape, pbytes = d["probe"]
-        pgbs = pbytes / (pms * 1e-3) / 1e9
-        line["roofline"]["read_probe"] = {
-            "what": "the same blocks read whole with no arithmetic (pa_probe_block_read), "
-                    "best of %d launch shapes" % len(PROBE_SHAPES),
-            "us": round(pms * 1e3, 3), "bytes": pbytes, "gbs": round(pgbs, 1),
-            "frac_of_peak": round(pgbs / HBM_PEAK_GBS, 4),
-            "waves_blocks_per_wg": list(pshape),
-            "kernel_frac_of_probe": round(d["kernel_gbs"] / pgbs, 4)}
-    if "mixed" in result:
-        m = result["mixed"]
-        pre = m["sub"]["prefill_rows"]
-        dec = m["sub"]["decode_rows"]
-        line["mixed_step"] = {
-            "workload": ("mixed chunked-prefill step, 8192 new tokens: 256 decode rows (context "
-                         "U[256,8192]) + 4 chunks of 1984 tokens (prior context U[0,4096]); "
-                         "32 q / 8 kv heads, head_size 128"),
-            "tokens_per_s": round(m["tokens_per_s"], 1), "unit": "tokens/s",
-            "ms_per_step": round(m["ms_step"], 4), "ms_forward_kernels": round(m["ms_fwd"], 4),
-            "kernel_avg_us": m["kernels"],
-            "prefill_rows": {"ms": round(pre["ms_fwd"], 4), "flops": pre["flops"],
-                             "kernel_avg_us": pre["kernels"],
-                             "tflops": round(pre["flops"] / (pre["ms_fwd"] * 1e-3) / 1e12, 2),
-                             "frac_of_bf16_peak": round(pre["flops"] / (pre["ms_fwd"] * 1e-3)
-                                                        / 1e12 / BF16_PEAK_TFLOPS, 4),
-                             # the tile kernel alone (events around each launch)
-                             "tile_kernel_frac_of_bf16_peak": round(
-                                 pre["flops"] / (pre["kernels"]["prefill"] * 1e-6) / 1e12
-                                 / BF16_PEAK_TFLOPS, 4) if "prefill" in pre["kernels"] else None},
-            "decode_rows": {"ms": round(dec["ms_fwd"], 4), "bytes": dec["bytes"],
-                            "kernel_avg_us": dec["kernels"],
-                            "gbs": round(dec["bytes"] / (dec["ms_fwd"] * 1e-3) / 1e9, 2),
-                            "frac_of_hbm_peak": round(dec["bytes"] / (dec["ms_fwd"] * 1e-3)
-                                                      / 1e9 / HBM_PEAK_GBS, 4)}}
-        if "value" not in line:
-            line.update(value=round(m["tokens_per_s"], 1), unit="tokens/s",
-                        ms_per_step=round(m["ms_step"], 5),
-                        config={"workload": line["mixed_step"]["workload"]})
-    for name, entry in others:
-        line.setdefault("other_workloads", {})[name] = entry
-    if "value" not in line and others:
-        name, entry = others[0]
-        line.update(value=entry["forward_gbs_logical"], unit="GB/s",
-                    ms_per_step=entry["ms_per_step"], config={"workload": entry["workload"]})
-    if not args.no_cpu and "decode" in result:
+    only = args.only
+    if only in ("mixed_decode", "mixed_prefill"):
+        line["workloads"] = {only: leg_sub(pa, args, dev, only)}
+        print(json.dumps(line), flush=True)
+        return 0
+    if only in (None, "decode"):
+        t_leg = time.perf_counter()
+        d = leg_decode(pa, args, dev)
+        progress(f"decode done in {time.perf_counter() - t_leg:.1f} s")
+        line.update(value=d["value"], unit="GB/s", ms_per_step=round(d["ms_step"], 5),
+                    config=d["config"], roofline=d["roofline"])
+        torch.cuda.empty_cache()
+    legs = (("mixed_step", "mixed", leg_mixed), ("long_decode", "long", leg_long),
+            ("prefix_shared", "prefix", leg_prefix), ("tiny", "tiny", leg_tiny),
+            ("spec_verify", "spec_decode", leg_spec))
+    for key, name, fn in legs:
+        if only not in (None, name):
+            continue
+        t_leg = time.perf_counter()
+        entry = fn(pa, args, dev)
+        progress(f"{key} done in {time.perf_counter() - t_leg:.1f} s")
+        torch.cuda.empty_cache()
+        if key == "mixed_step":
+            line["mixed_step"] = entry
+        else:
+            line.setdefault("workloads", {})[key] = entry
+    if "value" not in line:
+        # a single-workload profiling run: its own rate stands as the value
+        if "mixed_step" in line:
+            m = line["mixed_step"]
+            line.update(value=m["tokens_per_s"], unit="tokens/s", ms_per_step=m["ms_per_step"],
+                        config={"workload": m["workload"]})
+        else:
+            (key, e), = line["workloads"].items()
+            line.update(value=e["ms_per_step"], unit="ms", ms_per_step=e["ms_per_step"],
+                        higher_is_better=False, config={"workload": e["workload"]})
+    if not args.no_cpu and only in (None, "decode"):
+        t_leg = time.perf_counter()
         line["cpu_baseline"] = cpu_baseline(wl.config(2))
+        progress(f"cpu_baseline done in {time.perf_counter() - t_leg:.1f} s")
     print(json.dumps(line), flush=True)
     return 0
 
