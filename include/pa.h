@@ -231,6 +231,39 @@ int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mappi
                          size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * pa_write_and_forward without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is the library's own fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes, one per device (held until the process
+ * ends). Arguments, results and errors are those of pa_write_and_forward
+ * with workspace and workspace_bytes left out; the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).
+ *
+ *   - Sizes whose pa_forward_workspace_bytes(...) exceeds
+ *     PA_NOALLOC_SCRATCH_BYTES are rejected with PA_ERR_WORKSPACE before
+ *     anything is launched (the named workloads of this library need at
+ *     most about 33 MiB).
+ *   - The first call on a device, with that device current, looks up the
+ *     array's address and enqueues a fill kernel on `stream` that clears its
+ *     counter region; make that first call outside graph capture. Every
+ *     call leaves the counter region zero again.
+ *   - Every call on one device shares that device's array: calls that
+ *     overlap on one device (different streams, or host threads, without
+ *     ordering between them) race. Order them on one stream.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int pa_write_and_forward_noalloc(const void* k, const void* v, const int64_t* slot_mapping,
+                                 void* k_cache, void* v_cache, const void* q,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, float scale, void* out,
+                                 int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_query_len_hint, int32_t max_seq_len_hint,
+                                 uint32_t flags, void* stream);
+
+/*
  * Decode rows whose tables all begin with the same prefix_blocks blocks
  * (a shared prompt prefix; section "Prefix Caching": a cached block is
  * referenced by every request that shares it). The prefix's keys are

@@ -16,7 +16,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["cache_write", "forward", "write_and_forward", "forward_shared_prefix",
+__all__ = ["cache_write", "forward", "write_and_forward", "write_and_forward_noalloc",
+           "forward_shared_prefix",
            "forward_workspace_bytes",
            "validate_inputs",
            "kv_block_bytes", "last_error", "version", "library_path", "load_library",
@@ -27,6 +28,7 @@ FORWARD_SHARED_BLOCKS = 1  # PA_FORWARD_SHARED_BLOCKS
 WORKSPACE_COUNTER_BYTES = 256 * 1024  # PA_WORKSPACE_COUNTER_BYTES
 FORWARD_DECODE_EVEN_SHARES = 2  # PA_FORWARD_DECODE_EVEN_SHARES
 FORWARD_DECODE_PARTITIONED = 4  # PA_FORWARD_DECODE_PARTITIONED
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # PA_NOALLOC_SCRATCH_BYTES
 _SCHEDULE_FLAGS = {"even": FORWARD_DECODE_EVEN_SHARES, "partitioned": FORWARD_DECODE_PARTITIONED}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -78,6 +80,10 @@ SIGNATURES = {
     "pa_write_and_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                             _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I64,
                                             _I32, _I32, _P, _SZ, ctypes.c_uint32, _P]),
+    "pa_write_and_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                    ctypes.c_float, _P, _I32, _I32, _I32, _I32,
+                                                    _I32, _I32, _I32, _I64, _I32, _I32,
+                                                    ctypes.c_uint32, _P]),
     "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                           _I32, _I32, _P]),
     "pa_probe_block_read": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
@@ -347,6 +353,53 @@ def write_and_forward(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
     _check(load_library().pa_write_and_forward(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                                k_cache.data_ptr(), v_cache.data_ptr(),
                                                q.data_ptr(), *tail))
+    return out
+
+
+def write_and_forward_noalloc(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                              k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor,
+                              block_table: torch.Tensor, seq_lens: torch.Tensor,
+                              query_start_loc: torch.Tensor, scale: float, out: torch.Tensor,
+                              max_query_len: Optional[int] = None,
+                              max_seq_len: Optional[int] = None, shared_blocks: bool = False,
+                              decode_schedule: Optional[str] = None) -> torch.Tensor:
+    """``write_and_forward`` with the library's own fixed scratch array as
+    the workspace (pa_write_and_forward_noalloc): nothing is allocated, by
+    the library or here, so ``out`` must be given. For callers that cannot
+    allocate (graph capture, serving loops); calls that overlap on one
+    device race for the scratch."""
+    lib = load_library()
+    for n, t in (("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+    _dev_tensor("q", q, torch.bfloat16, 3)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(n, t, torch.bfloat16, 4)
+    _dev_tensor("block_table", block_table, torch.int32, 2)
+    _dev_tensor("seq_lens", seq_lens, torch.int32, 1)
+    _dev_tensor("query_start_loc", query_start_loc, torch.int32, 1)
+    _dev_tensor("out", out, torch.bfloat16, 3)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, Dc = k_cache.shape
+    S, MB = block_table.shape
+    if v_cache.shape != k_cache.shape or Dc != D or out.shape != q.shape:
+        raise ValueError("caches must be [NB, 16, Hkv, D] with q's head size; out q's shape")
+    if k.shape != v.shape or k.shape[0] != T or slot_mapping.shape[0] != T:
+        raise ValueError("k, v, slot_mapping and q disagree in token count")
+    if tuple(k.shape[1:]) != (Hkv, D):
+        raise ValueError("k must be [T, Hkv, D] matching the caches")
+    if seq_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("seq_lens must be [S] and query_start_loc [S+1]")
+    flags = FORWARD_SHARED_BLOCKS if shared_blocks else 0
+    if decode_schedule is not None:
+        if decode_schedule not in _SCHEDULE_FLAGS:
+            raise ValueError(f"decode_schedule must be one of {sorted(_SCHEDULE_FLAGS)}")
+        flags |= _SCHEDULE_FLAGS[decode_schedule]
+    _check(lib.pa_write_and_forward_noalloc(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+        query_start_loc.data_ptr(), float(scale), out.data_ptr(), T, S, Hq, Hkv, D, bs, MB, NB,
+        max_query_len or 0, max_seq_len or 0, flags, _stream(q)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -290,6 +291,61 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// pa_write_and_forward_noalloc: the same call with the library's own scratch
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// The workspace of pa_write_and_forward_noalloc: one array per device (each
+// device that runs the call holds its own copy until the process ends). In
+// host code `scratch` names a host-side stand-in, not device memory: host
+// code uses only the address hipGetSymbolAddress gives for the current
+// device, kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+// Zero fill of 32-bit words by a kernel (capture-safe, unlike a memset node).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch address. The first call on a device looks it
+// up (the device must be current) and clears the arrival-counter region on
+// `stream`, ahead of the forward launches enqueued after it; every later
+// call leaves that region zero.
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_and_forward_noalloc: device %d (at most %d)", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "pa_write_and_forward_noalloc: hipGetSymbolAddress(scratch)");
+    const int64_t words = PA_WORKSPACE_COUNTER_BYTES / 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
+                       stream, (uint32_t*)p, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward_noalloc: clearing scratch");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
 namespace {
 
 // The step's KV write when it travels with the forward (pa_write_and_forward).
@@ -311,7 +367,8 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
                  int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                  int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
-                 size_t workspace_bytes, uint32_t flags, void* stream) {
+                 size_t workspace_bytes, uint32_t flags, void* stream,
+                 bool static_scratch = false) {
   const uint32_t known =
       PA_FORWARD_SHARED_BLOCKS | PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED;
   if (flags & ~known)
@@ -349,6 +406,16 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   if (!pa::plan_workspace(num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size,
                           max_blocks_per_seq, max_query_len_hint, max_seq_len_hint, &w))
     return fail(PA_ERR_SHAPE, "pa_forward: cannot plan the workspace");
+  if (static_scratch) {
+    // pa_write_and_forward_noalloc: the library's fixed array is the workspace
+    if (w.total > kScratchBytes)
+      return fail(PA_ERR_WORKSPACE, "pa_write_and_forward_noalloc: these sizes need %zu bytes "
+                  "of scratch; its fixed size is %zu bytes (use pa_write_and_forward with a "
+                  "workspace)", w.total, kScratchBytes);
+    const int rc = device_scratch((hipStream_t)stream, &workspace);
+    if (rc != PA_OK) return rc;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < w.total)
     return fail(PA_ERR_WORKSPACE, "pa_forward: workspace of %zu bytes, %zu needed",
                 workspace ? workspace_bytes : (size_t)0, w.total);
@@ -430,6 +497,31 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   return PA_OK;
 }
 
+// pa_write_and_forward with a caller's workspace, or with the library's
+// fixed array (static_scratch: pa_write_and_forward_noalloc).
+int write_and_forward_impl(const void* k, const void* v, const int64_t* slot_mapping,
+                           void* k_cache, void* v_cache, const void* q,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, float scale, void* out,
+                           int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks,
+                           int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, void* stream,
+                           bool static_scratch) {
+  if (num_tokens > 0) {
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+      return fail(PA_ERR_NULL, "pa_write_and_forward: null k/v/slot_mapping/cache");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_ALIGN, "pa_write_and_forward: k and v must be 16-byte aligned");
+  }
+  const WriteArgs wr{k, v, slot_mapping, k_cache, v_cache};
+  return forward_impl(&wr, q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                      out, num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                      max_blocks_per_seq, num_blocks, max_query_len_hint, max_seq_len_hint,
+                      workspace, workspace_bytes, flags, stream, static_scratch);
+}
+
 }  // namespace
 
 extern "C" {
@@ -457,19 +549,30 @@ int pa_write_and_forward(const void* k, const void* v, const int64_t* slot_mappi
                          int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
                          size_t workspace_bytes, uint32_t flags, void* stream) {
   g_last_error.clear();
-  if (num_tokens > 0) {
-    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
-      return fail(PA_ERR_NULL, "pa_write_and_forward: null k/v/slot_mapping/cache");
-    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
-      return fail(PA_ERR_ALIGN, "pa_write_and_forward: k and v must be 16-byte aligned");
-  }
-  const WriteArgs wr{k, v, slot_mapping, k_cache, v_cache};
-  return forward_impl(&wr, q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
-                      out, num_tokens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
-                      max_blocks_per_seq, num_blocks, max_query_len_hint, max_seq_len_hint,
-                      workspace, workspace_bytes, flags, stream);
+  return write_and_forward_impl(k, v, slot_mapping, k_cache, v_cache, q, block_table, seq_lens,
+                                query_start_loc, scale, out, num_tokens, num_seqs, num_q_heads,
+                                num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                                num_blocks, max_query_len_hint, max_seq_len_hint, workspace,
+                                workspace_bytes, flags, stream, false);
 }
 
+// The same call with the library's fixed scratch array as the workspace.
+int pa_write_and_forward_noalloc(const void* k, const void* v, const int64_t* slot_mapping,
+                                 void* k_cache, void* v_cache, const void* q,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 const int32_t* query_start_loc, float scale, void* out,
+                                 int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_query_len_hint, int32_t max_seq_len_hint,
+                                 uint32_t flags, void* stream) {
+  g_last_error.clear();
+  return write_and_forward_impl(k, v, slot_mapping, k_cache, v_cache, q, block_table, seq_lens,
+                                query_start_loc, scale, out, num_tokens, num_seqs, num_q_heads,
+                                num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                                num_blocks, max_query_len_hint, max_seq_len_hint, nullptr, 0,
+                                flags, stream, true);
+}
 
 }  // extern "C"
 

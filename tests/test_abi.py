@@ -192,3 +192,31 @@ def test_profile_with_no_launches_is_empty(lib):
     # begin/end with nothing launched in between touches no HIP call
     pa.profile_begin()
     assert pa.profile_end() == {}
+
+
+def test_noalloc_rejects_sizes_past_its_scratch_before_launching(lib):
+    """Sizes that need more workspace than the fixed scratch array: a
+    PA_ERR_WORKSPACE error naming both sizes, with nothing launched (no
+    device is touched: the check is host arithmetic)."""
+    S, Hq, Hkv, D, MB = 4000, 64, 8, 128, 2048
+    need = pa.forward_workspace_bytes(S, S, Hq, Hkv, D, MB)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    rc = lib.pa_write_and_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          0.1, FAKE, S, S, Hq, Hkv, D, 16, MB, 1 << 20, 1, 0, 0,
+                                          None)
+    assert rc == -5
+    msg = pa.last_error()
+    assert str(need) in msg and str(pa.NOALLOC_SCRATCH_BYTES) in msg
+
+
+def test_noalloc_reports_argument_errors_like_the_workspace_call(lib):
+    args = [FAKE] * 9 + [0.1, FAKE, 8, 2, 32, 4, 64, 16, 4, 64, 0, 0, 0, None]
+    bad_block = list(args)
+    bad_block[16] = 32  # block_size
+    assert lib.pa_write_and_forward_noalloc(*bad_block) == -3
+    bad_group = list(args)
+    bad_group[13] = 3   # 32 q heads over 3 kv heads
+    assert lib.pa_write_and_forward_noalloc(*bad_group) == -2
+    empty = list(args)
+    empty[11] = 0       # no tokens: nothing to do, nothing launched
+    assert lib.pa_write_and_forward_noalloc(*empty) == 0
