@@ -222,12 +222,24 @@ def dist_us(t):
             "p90": round(t["ms_p90"] * 1e3, 3)}
 
 
+def graph_workspace(pa, inp: StepInputs) -> torch.Tensor:
+    """A workspace owned by the caller for captured steps (zeroed: its
+    counter region must start at zero), kept alive with the graphs."""
+    s = inp.spec
+    n = pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, s.num_q_heads, s.num_kv_heads,
+                                   s.head_size, s.max_blocks_per_seq,
+                                   max_seq_len=inp.hints["max_seq_len"],
+                                   max_query_len=inp.hints["max_query_len"])
+    return torch.zeros(n, dtype=torch.uint8, device=inp.k_cache.device)
+
+
 def run_graph_steps(pa, inp: StepInputs, steps: int, warmup: int) -> float:
     """The same steps captured once per block-table set in a HIP graph
     (torch.cuda.CUDAGraph over the library's launches) and replayed in turn;
     returns ms per step (HIP events around the replays on the current
     stream)."""
     spec = inp.spec
+    ws = graph_workspace(pa, inp)
     graphs = []
     for r in range(inp.rotations):
         st = inp.sets[r]
@@ -235,7 +247,7 @@ def run_graph_steps(pa, inp: StepInputs, steps: int, warmup: int) -> float:
         def step(st=st):
             pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
                                  st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
-                                 out=st["out"], **inp.hints)
+                                 out=st["out"], workspace=ws, **inp.hints)
         step()  # kernels loaded and the workspace allocated outside the capture
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -260,12 +272,13 @@ def run_graph_loop(pa, inp: StepInputs, steps: int, warmup: int) -> float:
     graph launch paid once per that many steps); returns ms per step (HIP
     events around the replays on the current stream)."""
     spec = inp.spec
+    ws = graph_workspace(pa, inp)
 
     def all_sets():
         for st in inp.sets:
             pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
                                  st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
-                                 out=st["out"], **inp.hints)
+                                 out=st["out"], workspace=ws, **inp.hints)
 
     all_sets()  # kernels loaded and the workspace allocated outside the capture
     torch.cuda.synchronize()

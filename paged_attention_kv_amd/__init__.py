@@ -201,14 +201,24 @@ def forward_workspace_bytes(num_tokens: int, num_seqs: int, num_q_heads: int, nu
 
 
 _workspaces: dict = {}
+# Workspaces replaced by larger ones stay alive for the life of the process:
+# a graph captured earlier still holds their addresses.
+_retired_workspaces: list = []
 
 
 def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                "the implicit workspace would have to grow during graph capture: pass a "
+                "workspace (forward_workspace_bytes(...) bytes, its first "
+                "WORKSPACE_COUNTER_BYTES zero) to calls made under capture")
         # zero-filled once: the leading counter region must start at zero
         # (every call leaves it zero)
+        if ws is not None:
+            _retired_workspaces.append(ws)
         ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws

@@ -107,27 +107,31 @@ __device__ __forceinline__ f32x2 load_coherent2(const float* p) {
 }
 
 // Hand-over of a split row between workgroups (every thread of the
-// workgroup calls it, after storing its partials with store_coherent2):
-// the stores are released at agent scope by the arrival counter's
-// read-modify-write (each wave first waits for its own stores, then the
-// workgroup barrier orders them before thread 0's release), and the
-// workgroup that arrives last (old value ncontrib - 1) acquires them with
-// the same read-modify-write and an agent-scope acquire fence in every
-// thread before it reads other workgroups' partials. The last arriver resets
-// the counter to zero. Returns true in every thread of the last workgroup.
+// workgroup calls it, after storing its partials with store_coherent2).
+// Each wave waits for its own stores, the workgroup barrier orders them
+// before thread 0's read-modify-write of the arrival counter, which releases
+// them at agent scope. The workgroup that arrives last (old value
+// ncontrib - 1) has read the value the others' release RMWs left (each RMW
+// continues the release sequences of the ones before it); its thread 0 takes
+// an agent-scope acquire fence, and the second barrier orders every thread's
+// later reads of the partials after it. Only the last arriver acquires, so
+// the others pay no cache invalidation. The last arriver resets the counter
+// (no other workgroup of this launch touches it again). Returns true in
+// every thread of the last workgroup.
 __device__ __forceinline__ bool count_in(int32_t* ctr, int ncontrib, int32_t* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == ncontrib - 1;
-    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     *flag = last;
   }
   __syncthreads();
-  const bool last = *flag != 0;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
+  return *flag != 0;
 }
 
 // Online-softmax state of one wave: O^T tiles (lane: d = 16*mi + 4*(l/16) + r,

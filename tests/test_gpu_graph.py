@@ -162,3 +162,36 @@ def test_graph_replays_of_the_shared_prefix_pass_match_eager():
         r, want = view.expect(q=q)
         assert_close(got.cpu()[r], want, f"shared prefix replay {i}")
         _ = (q.float() * 2).sum()
+
+
+def test_implicit_workspace_does_not_grow_under_capture():
+    """A call made under capture without a workspace of its own, whose sizes
+    need more than the implicit per-device workspace holds, raises before
+    launching anything (a larger workspace would leave graphs captured
+    earlier pointing at the old one); outside capture the workspace grows and
+    the old one is kept alive."""
+    pa._workspaces.clear()
+    small = wl.custom("ws_small", 32, 8, 128, rows=[(1, 100)], seed=300)
+    big = wl.custom("ws_big", 32, 8, 128, rows=[(1, 8000)] + [(1, 5)] * 2999, seed=301)
+    need = [pa.forward_workspace_bytes(s.num_tokens, s.num_seqs, 32, 8, 128,
+                                       s.max_blocks_per_seq) for s in (small, big)]
+    assert need[1] > need[0]
+    cs = wl.make_case(small, device=DEV)
+    cb = wl.make_case(big, device=DEV)
+
+    def fwd(c):
+        return pa.forward(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                          c.query_start_loc, c.scale)
+
+    fwd(cs)
+    torch.cuda.synchronize()
+    first = pa._workspaces[torch.cuda.current_device()]
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="graph capture"):
+        with torch.cuda.graph(g):
+            fwd(cb)
+    torch.cuda.synchronize()
+    fwd(cb)  # outside capture: grows
+    torch.cuda.synchronize()
+    assert pa._workspaces[torch.cuda.current_device()].numel() >= need[1]
+    assert any(w is first for w in pa._retired_workspaces)
