@@ -254,7 +254,8 @@ def run_graph_steps(pa, inp: StepInputs, steps: int, warmup: int) -> float:
         with torch.cuda.graph(g):
             step()
         graphs.append(g)
-    for i in range(warmup):
+    # every graph replayed (uploaded, first-launch costs paid) before timing
+    for i in range(max(warmup, 2 * len(graphs))):
         graphs[i % len(graphs)].replay()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -286,7 +287,7 @@ def run_graph_loop(pa, inp: StepInputs, steps: int, warmup: int) -> float:
     with torch.cuda.graph(g):
         all_sets()
     reps = max(1, steps // inp.rotations)
-    for _ in range(max(1, warmup // inp.rotations)):
+    for _ in range(max(2, warmup // inp.rotations)):
         g.replay()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)

@@ -34,6 +34,13 @@ def hipcc() -> str:
     return path
 
 
+# Per-file code generation options. The prefill tile kernels are scheduled
+# with the backend's iterative ILP strategy: it keeps more LDS operand reads
+# in flight ahead of the matrix instructions (fewer full LDS waits per tile)
+# at up to 254 VGPRs, still two waves per SIMD, and measured 3% faster on the
+# mixed step's prefill rows than the default strategy.
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
 # Host-only sources (the block manager / step planner) build with the host
 # compiler.
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
@@ -53,7 +60,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         if src.endswith(".cpp"):
             cmd = [shutil.which("g++") or "g++", *HOST_FLAGS, "-c", src, "-o", obj]
         else:
-            cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+            cmd = [cc, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
