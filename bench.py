@@ -55,6 +55,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROTATIONS = 8
 COPY_MIB = 512
+MIXED_WARMUP = 40  # untimed steps before the mixed step is timed (see leg_mixed)
 GRAPH_NOTE = ("the same step captured in a HIP graph per block-table set and replayed "
               "(value uses eager launches)")
 
@@ -161,7 +162,8 @@ def percentile(xs, f):
     return v[lo] + (v[hi] - v[lo]) * (x - lo)
 
 
-def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool = False):
+def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool = False,
+              serial: bool = False):
     """Time `steps` steps (KV write + forward). Pass 1 is bracketed by
     synchronize and timed with HIP events on the launch stream, with nothing
     else inside: the step time. Pass 2 records an event between consecutive
@@ -170,7 +172,8 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool 
     the steps with the library's kernel timing on (pa.profile_begin/end: HIP
     events around every kernel launch on its stream). Returns a dict:
     ms_step, ms_median, ms_p10, ms_p90, kernels {class: mean ms per launch},
-    counts {class: launches per step}, ms_fwd (forward kernels per step)."""
+    counts {class: launches per step}, ms_fwd (forward kernels per step).
+    serial: a mixed batch's launches stay on one stream (PA_FORWARD_SERIAL)."""
     spec = inp.spec
 
     def step(i):
@@ -184,7 +187,7 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool 
             return
         pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
                              st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
-                             out=st["out"], **inp.hints)
+                             out=st["out"], serial=serial, **inp.hints)
 
     for i in range(warmup):
         step(i)
@@ -526,7 +529,12 @@ def leg_mixed(pa, args, dev):
     matrix-core use."""
     spec = wl.config(3)
     inp = StepInputs(spec, 1, dev)
-    t = run_steps(pa, inp, args.steps, args.warmup)
+    # With the prefill tiles running beside the decode launch, the first
+    # ~20-30 steps after a start or an idle pause run 5-15% slower before the
+    # step time settles; the leg times the settled steps.
+    warm = max(args.warmup, MIXED_WARMUP)
+    t = run_steps(pa, inp, args.steps, warm)
+    t_ser = run_steps(pa, inp, args.steps, warm, serial=True)
     dec_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] == 1]
     pre_rows = [s for s in range(spec.num_seqs) if spec.q_lens[s] > 1]
     del inp
@@ -552,6 +560,13 @@ def leg_mixed(pa, args, dev):
         "ms_per_step": round(t["ms_step"], 4), "step_us": dist_us(t),
         "ms_forward_kernels": round(t["ms_fwd"], 4),
         "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t["kernels"].items()},
+        "warmup_steps": warm,
+        "overlap": ("prefill launches on the library's second stream beside the decode "
+                    "launch (160 even shares); ms_forward_kernels sums kernels that overlap"),
+        "serial": {"ms_per_step": round(t_ser["ms_step"], 4), "step_us": dist_us(t_ser),
+                   "tokens_per_s": round(spec.num_tokens / (t_ser["ms_step"] * 1e-3), 1),
+                   "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in t_ser["kernels"].items()},
+                   "note": "the same step with PA_FORWARD_SERIAL (one stream, 256 shares)"},
         "prefill_rows": {
             "ms": round(pre_ms, 4), "flops": pre["flops"],
             "kernel_avg_us": {k: round(v * 1e3, 3) for k, v in pre["t"]["kernels"].items()},

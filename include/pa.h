@@ -180,11 +180,30 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
  *       EVEN_SHARES falls back to partitions when num_seqs > 4096. The
  *       results agree to rounding order; each schedule is deterministic.
  *
+ *   PA_FORWARD_SERIAL
+ *       keep every launch of a mixed batch on `stream`, one part after the
+ *       other (see below). The results are the same either way up to the
+ *       decode rows' rounding order (their shares differ).
+ *
  * Unknown flag bits, or both schedule flags, return PA_ERR_UNSUPPORTED.
+ *
+ * Mixed batches (section "Scheduler": one step holds decode rows, bound by
+ * memory bandwidth, and prefill rows, bound by compute): when the decode
+ * rows take even shares and num_tokens - num_seqs >= 1024, the prefill
+ * launches run on a second stream that the library makes for the device on
+ * the first such call (default priority; kept until the process ends),
+ * forked from `stream` after the call's cache write and joined back into
+ * `stream` by events before the call returns, while the decode's shares
+ * (160 of them, PA_MIXED_DECODE_WGS overrides) run on `stream` and leave
+ * CUs to the prefill tiles. Work enqueued on `stream` after the call still
+ * sees all of its results. Calls made while `stream` is being captured
+ * into a graph, calls with PA_FORWARD_SERIAL, pa_write_and_forward_noalloc
+ * and every process with PA_MIXED_OVERLAP=0 keep all launches on `stream`.
  */
 #define PA_FORWARD_SHARED_BLOCKS 1u
 #define PA_FORWARD_DECODE_EVEN_SHARES 2u
 #define PA_FORWARD_DECODE_PARTITIONED 4u
+#define PA_FORWARD_SERIAL 8u
 
 int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, const int32_t* seq_lens,

@@ -28,6 +28,7 @@ FORWARD_SHARED_BLOCKS = 1  # PA_FORWARD_SHARED_BLOCKS
 WORKSPACE_COUNTER_BYTES = 256 * 1024  # PA_WORKSPACE_COUNTER_BYTES
 FORWARD_DECODE_EVEN_SHARES = 2  # PA_FORWARD_DECODE_EVEN_SHARES
 FORWARD_DECODE_PARTITIONED = 4  # PA_FORWARD_DECODE_PARTITIONED
+FORWARD_SERIAL = 8  # PA_FORWARD_SERIAL
 NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # PA_NOALLOC_SCRATCH_BYTES
 _SCHEDULE_FLAGS = {"even": FORWARD_DECODE_EVEN_SHARES, "partitioned": FORWARD_DECODE_PARTITIONED}
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -225,7 +226,8 @@ def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
 
 
 def _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out,
-                  max_query_len, max_seq_len, workspace, shared_blocks, decode_schedule):
+                  max_query_len, max_seq_len, workspace, shared_blocks, decode_schedule,
+                  serial=False):
     """Checks and marshals the arguments shared by pa_forward_ex and
     pa_write_and_forward: returns (q .. out pointers and sizes .. stream), out."""
     lib = load_library()
@@ -249,6 +251,8 @@ def _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, s
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     flags = FORWARD_SHARED_BLOCKS if shared_blocks else 0
+    if serial:
+        flags |= FORWARD_SERIAL
     if decode_schedule is not None:
         if decode_schedule not in _SCHEDULE_FLAGS:
             raise ValueError(f"decode_schedule must be one of {sorted(_SCHEDULE_FLAGS)}")
@@ -271,7 +275,8 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
             workspace: Optional[torch.Tensor] = None,
             shared_blocks: bool = False,
-            decode_schedule: Optional[str] = None) -> torch.Tensor:
+            decode_schedule: Optional[str] = None,
+            serial: bool = False) -> torch.Tensor:
     """Paged attention of the flattened batch (q [T, Hq, D] bf16) over the
     paged caches; returns ``out`` ([T, Hq, D] bf16). ``max_query_len`` and
     ``max_seq_len`` are optional host upper bounds that shrink the launch
@@ -280,10 +285,14 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     per-device cache when omitted. ``shared_blocks`` tells the library that
     some blocks appear in several rows' tables (prefix caching); results are
     the same either way. ``decode_schedule`` ("even" or "partitioned")
-    forces the decode rows' schedule; by default the library picks."""
+    forces the decode rows' schedule; by default the library picks.
+    ``serial`` keeps a mixed batch's prefill and decode launches on the
+    current stream one after the other (by default a large mixed batch runs
+    them side by side, the prefill on a second stream of the library's,
+    joined back before the call returns)."""
     tail, out = _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
                               out, max_query_len, max_seq_len, workspace, shared_blocks,
-                              decode_schedule)
+                              decode_schedule, serial)
     _check(load_library().pa_forward_ex(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                          *tail))
     return out
@@ -346,10 +355,11 @@ def write_and_forward(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
                       max_query_len: Optional[int] = None, max_seq_len: Optional[int] = None,
                       workspace: Optional[torch.Tensor] = None,
                       shared_blocks: bool = False,
-                      decode_schedule: Optional[str] = None) -> torch.Tensor:
+                      decode_schedule: Optional[str] = None,
+                      serial: bool = False) -> torch.Tensor:
     """``cache_write`` then ``forward`` in one call (pa_write_and_forward):
     with ``max_query_len=1`` (decode rows only) one launch writes the new
-    tokens and attends. Returns ``out``."""
+    tokens and attends. ``serial`` as for ``forward``. Returns ``out``."""
     for n, t in (("k", k), ("v", v)):
         _dev_tensor(n, t, torch.bfloat16, 3)
     _dev_tensor("slot_mapping", slot_mapping, torch.int64, 1)
@@ -359,7 +369,7 @@ def write_and_forward(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tens
         raise ValueError("k must be [T, Hkv, D] matching the caches")
     tail, out = _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
                               out, max_query_len, max_seq_len, workspace, shared_blocks,
-                              decode_schedule)
+                              decode_schedule, serial)
     _check(load_library().pa_write_and_forward(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
                                                k_cache.data_ptr(), v_cache.data_ptr(),
                                                q.data_ptr(), *tail))

@@ -95,7 +95,10 @@ struct PrefillPlan {
   int32_t* tiles_b;      // [bound_b][2]
   int32_t* counts;       // [2] tiles the planner put in lists A and B
 };
-hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
+// The planner (one workgroup), then the tiles it listed; the tiles may go to
+// another stream ordered after the planner.
+hipError_t launch_prefill_plan(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
+hipError_t launch_prefill_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
 // Query tokens per prefill tile for a given group size (MFMA rows / G), for
 // tiles whose rows see many keys (list A) and few (list B).
 int32_t prefill_tile_queries(int32_t group);

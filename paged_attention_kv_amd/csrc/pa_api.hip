@@ -178,6 +178,26 @@ int32_t decode_prefetch(int32_t head_size) {
   return v ? v : 2;
 }
 
+// Mixed batches: decode rows on even shares are bound by HBM bandwidth and
+// prefill rows by the matrix cores, so the two parts run side by side (the
+// prefill launches on a second stream). The decode then takes fewer shares
+// than CUs, leaving CUs to the prefill tiles; on the mixed 8192-token step
+// 160 shares measured best (128..224 swept), and the decode rows alone lose
+// only ~10% at 160 shares since ~200 CUs already carry HBM's rate. Batches
+// with fewer prefill tokens than kOverlapMinPrefillTokens run one part after
+// the other. PA_MIXED_OVERLAP=0 turns the overlap off; PA_MIXED_DECODE_WGS
+// sets the decode's shares (for sweeps).
+constexpr int32_t kOverlapDecodeWgs = 160;
+constexpr int64_t kOverlapMinPrefillTokens = 1024;
+bool mixed_overlap_enabled() {
+  static const int v = env_int("PA_MIXED_OVERLAP", 0, 1, 1);
+  return v == 1;
+}
+int32_t mixed_decode_wgs() {
+  static const int v = env_int("PA_MIXED_DECODE_WGS", 1, kStreamMaxWgs, kOverlapDecodeWgs);
+  return v;
+}
+
 }  // namespace
 
 namespace pa {
@@ -348,6 +368,59 @@ int device_scratch(hipStream_t stream, void** out) {
 
 namespace {
 
+// The second stream of a device on which a mixed batch's prefill launches
+// run beside its decode launch, with the events that fork it from and join
+// it back to the caller's stream. Made on the first mixed call on the device
+// (default priority, non-blocking); kept until the process ends. Calls hold
+// g_side_mu from the fork to the join, so calls from several host threads
+// take turns on it.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+// The current device's side stream (g_side_mu held), or nullptr when it
+// cannot be had (the call then runs its parts one after the other).
+SideStream* side_stream_locked() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  SideStream& sd = g_side[dev];
+  if (!sd.s) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      if (j) (void)hipEventDestroy(j);
+      if (f) (void)hipEventDestroy(f);
+      if (s) (void)hipStreamDestroy(s);
+      return nullptr;
+    }
+    sd.s = s;
+    sd.fork = f;
+    sd.join = j;
+  }
+  return &sd;
+}
+
+// True when `st` is being captured into a graph (or its state cannot be
+// read): such calls keep every launch on `st`.
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 // The step's KV write when it travels with the forward (pa_write_and_forward).
 struct WriteArgs {
   const void* k;
@@ -369,8 +442,8 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
                  int32_t max_query_len_hint, int32_t max_seq_len_hint, void* workspace,
                  size_t workspace_bytes, uint32_t flags, void* stream,
                  bool static_scratch = false) {
-  const uint32_t known =
-      PA_FORWARD_SHARED_BLOCKS | PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED;
+  const uint32_t known = PA_FORWARD_SHARED_BLOCKS | PA_FORWARD_DECODE_EVEN_SHARES |
+                         PA_FORWARD_DECODE_PARTITIONED | PA_FORWARD_SERIAL;
   if (flags & ~known)
     return fail(PA_ERR_UNSUPPORTED, "pa_forward_ex: unknown flags 0x%x", flags);
   if ((flags & PA_FORWARD_DECODE_EVEN_SHARES) && (flags & PA_FORWARD_DECODE_PARTITIONED))
@@ -456,8 +529,25 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward cache write launch");
   }
 
-  if (a.max_query_len > w.qmax) {
-    pa::PrefillPlan pp;
+  // A mixed batch on even shares with enough prefill tokens (num_tokens -
+  // num_seqs of them at least) runs its prefill tiles on the side stream,
+  // forked after the cache write and the tile planner and joined before the
+  // call returns; not under graph capture, and not for the no-allocation
+  // entry point (the side stream is made on first use).
+  const bool has_prefill = a.max_query_len > w.qmax;
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  if (has_prefill && dp.stream && !static_scratch && !(flags & PA_FORWARD_SERIAL) &&
+      mixed_overlap_enabled() && (int64_t)num_tokens - num_seqs >= kOverlapMinPrefillTokens &&
+      !capturing(st)) {
+    side_lock.lock();
+    side = side_stream_locked();
+    if (!side) side_lock.unlock();
+  }
+  // The planner runs on the caller's stream (one workgroup: beside the
+  // decode launch it would wait behind the decode's loads), then the fork.
+  pa::PrefillPlan pp{};
+  if (has_prefill) {
     pp.tile_queries = w.tile_queries;
     pp.split_tile_queries = pa::prefill_split_tile_queries(num_q_heads / num_kv_heads);
     const int64_t by_hint_a =
@@ -469,10 +559,30 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     pp.tiles_a = (int32_t*)(ws + w.off_tiles_a);
     pp.tiles_b = (int32_t*)(ws + w.off_tiles_b);
     pp.counts = (int32_t*)(ws + w.off_counts);
-    hipError_t e = pa::launch_prefill(a, pp, st);
-    if (e != hipSuccess) return hip_fail(e, "pa_forward prefill launch");
+    hipError_t e = pa::launch_prefill_plan(a, pp, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_forward prefill planner launch");
   }
-  dp.stream_wgs = w.stream_wgs;
+  hipStream_t pst = st;  // the prefill tiles' stream
+  if (side) {
+    hipError_t e = hipEventRecord(side->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return hip_fail(e, "pa_forward: forking the prefill stream");
+    pst = side->s;
+  }
+  // Joins the side stream back into the caller's stream (every return after
+  // the fork passes through it, so no launch is left unordered).
+  auto join = [&](int rc) {
+    if (!side) return rc;
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+    if (e != hipSuccess && rc == PA_OK) return hip_fail(e, "pa_forward: joining the prefill stream");
+    return rc;
+  };
+  if (has_prefill) {
+    hipError_t e = pa::launch_prefill_tiles(a, pp, pst);
+    if (e != hipSuccess) return join(hip_fail(e, "pa_forward prefill launch"));
+  }
+  dp.stream_wgs = side ? std::min(w.stream_wgs, mixed_decode_wgs()) : w.stream_wgs;
   dp.stream_heads = w.stream_heads;
   dp.part_tokens = w.part_tokens;
   dp.num_parts_max = w.num_parts_max;
@@ -493,8 +603,8 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   dp.k_cache_w = fused ? wr->k_cache : nullptr;
   dp.v_cache_w = fused ? wr->v_cache : nullptr;
   hipError_t e = pa::launch_decode(a, dp, st);
-  if (e != hipSuccess) return hip_fail(e, "pa_forward decode launch");
-  return PA_OK;
+  if (e != hipSuccess) return join(hip_fail(e, "pa_forward decode launch"));
+  return join(PA_OK);
 }
 
 // pa_write_and_forward with a caller's workspace, or with the library's

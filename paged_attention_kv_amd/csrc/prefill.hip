@@ -672,7 +672,7 @@ int32_t prefill_split_tiles_per_row(int32_t group) {
   return (kSplitKeys + bq - 1) / bq;
 }
 
-hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream) {
+hipError_t launch_prefill_plan(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream) {
   if (p.bound_a <= 0 && p.bound_b <= 0) return hipSuccess;
   profile_begin(PA_KERNEL_PLAN, stream);
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
@@ -680,8 +680,11 @@ hipError_t launch_prefill(const ForwardArgs& a, const PrefillPlan& p, hipStream_
                      p.split_tile_queries, p.tiles_a,
                      p.bound_a, p.tiles_b, p.bound_b, p.counts);
   profile_end(PA_KERNEL_PLAN, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream) {
+  if (p.bound_a <= 0 && p.bound_b <= 0) return hipSuccess;
   switch (a.head_size) {
     case 64: return launch_tiles_d<64>(a, p, stream);
     case 128: return launch_tiles_d<128>(a, p, stream);

@@ -99,8 +99,11 @@ def test_forward_rejects_bad_arguments(lib):
     assert fw(lib, T=0) == 0              # empty batch: no launch
     # unknown option flags are rejected before anything else happens
     assert lib.pa_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 8, 2, 32, 4, 64, 16,
-                             4, 64, 0, 0, FAKE, 1 << 30, 8, None) == -3
+                             4, 64, 0, 0, FAKE, 1 << 30, 16, None) == -3
     assert "unknown flags" in pa.last_error()
+    # PA_FORWARD_SERIAL (8) is a known flag: an empty batch with it succeeds
+    assert lib.pa_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 0, 2, 32, 4, 64, 16,
+                             4, 64, 0, 0, FAKE, 1 << 30, 8 | 1, None) == 0
     # both decode schedules at once
     assert lib.pa_forward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.125, FAKE, 8, 2, 32, 4, 64, 16,
                              4, 64, 0, 0, FAKE, 1 << 30, 6, None) == -3

@@ -195,3 +195,49 @@ def test_implicit_workspace_does_not_grow_under_capture():
     torch.cuda.synchronize()
     assert pa._workspaces[torch.cuda.current_device()].numel() >= need[1]
     assert any(w is first for w in pa._retired_workspaces)
+
+
+def test_graph_of_a_large_mixed_step_keeps_one_stream():
+    """A mixed batch large enough for its prefill to run on the library's
+    second stream eagerly keeps every launch on the capturing stream under
+    capture: each replay gives the bits of the eager call with
+    PA_FORWARD_SERIAL and matches the oracle."""
+    rows = [(1, 256 + (97 * i) % 1800) for i in range(300)] + [(700, 300), (900, 0)]
+    spec = wl.custom("graph_mixed_large", 32, 8, 128, rows=rows, seed=440)
+    assert spec.num_tokens - spec.num_seqs >= 1024
+    print(f"\n[case] graph of a large mixed step: S={spec.num_seqs} T={spec.num_tokens}",
+          flush=True)
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    hints = dict(max_query_len=max(spec.q_lens), max_seq_len=max(spec.seq_lens))
+    ws = torch.zeros(pa.forward_workspace_bytes(spec.num_tokens, spec.num_seqs, 32, 8, 128,
+                                                spec.max_blocks_per_seq, **hints),
+                     dtype=torch.uint8, device=DEV)
+    q, k, v = case.q.clone(), case.k.clone(), case.v.clone()
+    out = torch.empty_like(q)
+
+    def step(o, **kw):
+        pa.write_and_forward(k, v, case.slot_mapping, case.k_cache, case.v_cache, q,
+                             case.block_table, case.seq_lens, case.query_start_loc, case.scale,
+                             out=o, workspace=ws, **hints, **kw)
+
+    step(out)  # warm up outside the capture (kernels loaded, side stream made)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    ref = torch.empty_like(out)
+    for i in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+        k.copy_(torch.randn(k.shape, generator=gen, device=DEV).to(k.dtype))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        step(ref, serial=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        r, want = view.expect(q=q, k=k, v=v)
+        assert_close(got.cpu()[r], want, f"large mixed replay {i}")
+        _ = (q.float() * 2).sum()
+    assert int(ws[:pa.WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0
