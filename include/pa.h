@@ -21,12 +21,16 @@
  *   - Tensors are row-major and contiguous; "device" pointers point to HIP
  *     device memory of the current device; element type bf16 unless stated.
  *   - The caller owns every buffer, including the workspace. The library
- *     keeps no pointer after a call returns and allocates nothing on the hot
- *     path (pa_cache_write, pa_forward).
- *   - pa_cache_write and pa_forward only enqueue work on `stream` (a
+ *     keeps no pointer to them after a call returns and allocates no device
+ *     memory on the hot path (pa_cache_write, pa_forward); its only state is
+ *     a second stream and two events per device, made by the first large
+ *     mixed call (see pa_forward_ex).
+ *   - pa_cache_write and pa_forward only enqueue work ordered on `stream` (a
  *     hipStream_t; NULL = the null stream) and return: no device-to-host
- *     copy, no synchronisation. Call pa_cache_write for a step's tokens
- *     before pa_forward on the same stream.
+ *     copy, no synchronisation. A large mixed batch runs part of its work
+ *     on the second stream, forked from and joined back into `stream`
+ *     within the call. Call pa_cache_write for a step's tokens before
+ *     pa_forward on the same stream.
  *   - Host-known arguments are checked before anything is launched; a
  *     negative pa_status is returned and pa_last_error() describes it.
  *     Device-resident metadata (slots, lengths, tables) is trusted on the hot
