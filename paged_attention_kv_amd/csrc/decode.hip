@@ -14,18 +14,25 @@
 //                                                          K straight from HBM)
 //   O^T[D x 16 heads]       += V^T[D x 16] . P^T[16 x 16] (16x16x16 bf16 MFMA,
 //                                                          V transposed via LDS)
-// The S^T accumulator layout (lane: head l%16, tokens 4*(l/16)+r) is exactly
-// the B operand layout of the second product, so P never leaves registers.
-// Blocks stream through a ring of NBUF register buffers whose loads are
-// issued unconditionally (indices clamped), so the compiler's wait counts
-// only ever wait for the block being consumed. Softmax: scores are kept in
-// log2 units against a per-head reference max m, re-referenced (one max
-// across the four 16-lane groups, accumulators rescaled) only when a score
-// exceeds it by more than 2^kLazy; weights stay <= 2^kLazy, which bf16 hi+lo
-// parts and fp32 accumulators carry without loss. Several waves of a
-// workgroup may hold partial states of one (row, KV head); they are merged
-// through LDS: M = max m_w, l = sum 2^(m_w - M) l_w, o = sum 2^(m_w - M) o_w,
-// in wave order.
+// Each K load covers whole 128-byte lines of 8 tokens (a line fetched by two
+// instructions that each take half of it measured ~30% slower at low load);
+// the QK products take each line as two 32-element rows of the A operand and
+// add the pair, which leaves lane group grp with the scores of tokens 2*grp,
+// 2*grp+1, 8+2*grp and 9+2*grp. V rows are placed in LDS so that the
+// transpose reads give the same group those tokens, so P goes from the score
+// registers into the B operand of the second product without moving between
+// lanes. Blocks stream through a ring of NBUF register buffers whose loads
+// are issued unconditionally (indices clamped), so the compiler's wait counts
+// only ever wait for the block being consumed; blocks wholly inside every
+// query column's visible range take a path with no masks. Softmax: scores are
+// kept in log2 units against a per-head reference max m, re-referenced (one
+// max across the four 16-lane groups, accumulators rescaled) only when a
+// score exceeds it by more than 2^kLazy; weights stay <= 2^kLazy. Rows of at
+// most kSplitKeys keys pass the weights to PV as bf16 hi + lo parts (about
+// 2^-17 relative); longer rows as one bf16 part, their weight sums adding the
+// same rounded values. Several waves of a workgroup may hold partial states
+// of one (row, KV head); they are merged through LDS: M = max m_w, l = sum
+// 2^(m_w - M) l_w, o = sum 2^(m_w - M) o_w, in wave order.
 //
 // Two schedules:
 //  * stream (decode_stream_kernel): one persistent workgroup per CU takes an
@@ -54,9 +61,14 @@ namespace pa {
 namespace {
 
 constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
+// Rows of at most this many keys keep the weights to about 2^-17 (bf16 hi +
+// lo parts); longer rows take one bf16 part, as the prefill tiles do.
+constexpr int kSplitKeys = 128;
 // Fourth word of a raw buffer resource on gfx9-family chips: 32-bit data
 // format, so buffer loads move raw bytes.
 constexpr int kBufferWordFlags = 0x00020000;
+// Cache-policy bit of a buffer load that marks it nontemporal (streaming).
+constexpr int kBufferNt = 2;
 
 template <int D>
 struct DecodeShape {
@@ -75,10 +87,9 @@ struct DecodeShape {
   static_assert(kMergeCols * (kMergeRow * 4 + 8) <= kLdsWave * 2, "merge stage fits in LDS");
 };
 
-// Most waves per decode workgroup: as many as fit on a CU at the kernel's
-// register use (<= 128 VGPRs: 4 waves per SIMD; <= 168: 3). The fused-write
-// variants beyond D = 64 with two blocks in flight need more registers than
-// 168 and take at most 8 waves (<= 256 VGPRs), so they do not spill.
+// Most waves per partitioned decode workgroup, which sets the kernel's
+// register budget (<= 128 VGPRs at 16 waves, 4 per SIMD; <= 168 at 12; <= 256
+// at 8). Sweeps of 2..16 waves found four best on every workload.
 template <int D, int NBUF, bool kWrite = false>
 constexpr int max_waves() { return (D == 64 && NBUF == 2) ? 16 : (kWrite ? 8 : 12); }
 
@@ -140,13 +151,14 @@ template <int D>
 struct WaveAcc {
   f32x4 o[D / 16];
   float m;
-  float lsum;
+  float lsum;  // the lane's tokens' weights; after finish(), the column's
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int mi = 0; mi < D / 16; ++mi) o[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
     lsum = 0.f;
   }
+  __device__ __forceinline__ void finish() { lsum = sum_across_groups(lsum); }
 };
 
 // Q^T as the B operand: lane holds query column hl (< ncols, else zeros),
@@ -192,21 +204,53 @@ __device__ __forceinline__ int64_t first_lane64(int64_t x) {
 // k of `ids`, its first token is tok0 + k * tok_step, and tokens >= tok_end
 // are masked (their V rows zeroed). col_lim (per lane: its query column's
 // last visible key, >= tok_end - 1 for a single-token row) masks the tail
-// of a row with several query tokens causally. kbase / vbase point at the
-// head's slice of block 0 (kbase already offset to the lane's K row and
-// chunk); vl is the wave's LDS slice. With kNew, token nt.tok is read from
-// nt.k / nt.v.
-template <int D, int NBUF, bool kStreamV, bool kNew = false>
-__device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv)[D / 32], int ids,
-                                              int nk, int tok0, int tok_step, int tok_end,
-                                              const uint16_t* __restrict__ kbase,
-                                              const uint16_t* __restrict__ vbase, int64_t kv_row,
-                                              uint16_t* vl, float scale_log2, int lane,
-                                              NewToken nt = NewToken{-1, nullptr, nullptr, -1},
-                                              int col_lim = INT32_MAX) {
+// of a row with several query tokens causally; full_end (wave-uniform,
+// <= tok_end and <= every lane's col_lim + 1) is where masking can start:
+// a block wholly below it takes the unmasked path. kbase / vbase point at
+// the head's slice of the cache (element g * D of block 0); vl is the
+// wave's LDS slice. split_p: the weights enter PV as bf16 hi + lo parts
+// (rows with few keys, where each weight carries much of an output), else
+// as one bf16 part. With kNew, token nt.tok is read from nt.k / nt.v.
+template <int D, int NBUF, bool kStreamV, bool kNew, bool kSplit>
+__device__ __forceinline__ void stream_blocks_impl(WaveAcc<D>& acc, const bf16x8 (&qv)[D / 32],
+                                                   int ids, int nk, int tok0, int tok_step,
+                                                   int tok_end, int full_end,
+                                                   const uint16_t* __restrict__ kbase,
+                                                   const uint16_t* __restrict__ vbase,
+                                                   int64_t kv_row, uint16_t* vl, float scale_log2,
+                                                   int lane, NewToken nt, int col_lim) {
   using Sh = DecodeShape<D>;
   const int hl = lane & 15;
   const int grp = lane >> 4;
+
+  // K load j covers 8 tokens' whole 128-byte lines (tokens kt(j) .. +7,
+  // elements 64 * kl(j) .. +63 of each): lane (hl, grp) takes token
+  // kt(j) + hl/2, elements 64*kl(j) + 32*(hl%2) + 8*grp .. +7, so every line
+  // is fetched by one instruction. The lane's 16 bytes are the A operand of
+  // a 16x16x32 product whose row hl is half hl%2 of that token's line: the
+  // product with q's k-block 2*kl(j) is valid for even rows, with k-block
+  // 2*kl(j) + 1 for odd rows, and a token's score is the sum of its two
+  // rows. V: 16-byte chunk c*64 + lane of the head's 16 rows, chunk c one
+  // fixed stride after chunk 0. A block's loads are buffer loads from a base
+  // the wave computes once per block on the scalar unit, so the per-block
+  // address work is one lane read, a 32 x 32-bit product and two 64-bit adds.
+  const uint32_t blk_bytes = (uint32_t)(kBlock * kv_row * 2);
+  const int koff = (int)(((hl / 2) * kv_row + 32 * (hl % 2) + 8 * grp) * 2);
+  auto kt = [](int j) { return 8 * (j % 2); };  // first token of K load j
+  auto kl = [](int j) { return j / 2; };        // its 64-element line
+  const int voff = (int)(((lane / (D / 8)) * kv_row + (lane % (D / 8)) * 8) * 2);
+  constexpr int kVRows = kWave / (D / 8);             // rows per V chunk
+  const int vstride = (int)(kVRows * kv_row * 2);      // bytes between V chunks
+  const int nrec = (int)blk_bytes;  // loads stay inside the block
+  // The block (k index) holding the newest token when it is one of ours.
+  int knew = -1;
+  if constexpr (kNew) {
+    const int tb = nt.tok & ~(kBlock - 1);
+    if (nt.tok >= 0 && tb >= tok0 && (tb - tok0) % tok_step == 0) {
+      const int kk = (tb - tok0) / tok_step;
+      knew = kk < nk ? kk : -1;
+    }
+  }
 
   // Loads block min(k, nk-1): always issued, so the wait counts stay exact.
   // Unless blocks are shared between rows, V goes through nontemporal
@@ -215,30 +259,30 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
   // two halves of one 128-byte line, which streaming loads re-fetch.
   auto load_block = [&](int k, u32x4 (&kk)[Sh::kKChunks], u32x4 (&vv)[Sh::kVChunks]) {
     const int kc = min(k, nk - 1);
-    const int64_t blk = __builtin_amdgcn_readlane(ids, kc);
-    const int64_t boff = blk * kBlock * kv_row;
-    const u32x4* kp = (const u32x4*)(kbase + boff);
+    const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(ids, kc) * blk_bytes;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)kbase + off), (short)0, nrec, kBufferWordFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)vbase + off), (short)0, nrec, kBufferWordFlags);
 #pragma unroll
-    for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = kp[4 * i];
+    for (int j = 0; j < Sh::kKChunks; ++j)
+      kk[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          kr, koff, (int)((kt(j) * kv_row + 64 * kl(j)) * 2), 0);
 #pragma unroll
-    for (int c = 0; c < Sh::kVChunks; ++c) {
-      const int idx = c * kWave + lane;
-      const u32x4* vp = (const u32x4*)(vbase + boff + (idx / (D / 8)) * kv_row + (idx % (D / 8)) * 8);
-      vv[c] = kStreamV ? __builtin_nontemporal_load(vp) : *vp;
-    }
+    for (int c = 0; c < Sh::kVChunks; ++c)
+      vv[c] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff, c * vstride,
+                                                     kStreamV ? kBufferNt : 0);
     if constexpr (kNew) {
       // One block of the row holds its newest token: the wave that streams
       // it reads the slot here, long after its load returned, and then
-      // replaces that token's row with the step's own K and V. Both tests
-      // are wave-uniform branches, so every other block pays two scalar
-      // instructions after its loads.
-      const int tokb = tok0 + kc * tok_step;
-      if (tokb == (nt.tok & ~(kBlock - 1)) && first_lane64(nt.slot) >= 0) {
-        const int r = nt.tok - tokb;  // the token's row in the block
-        if (hl == r) {
+      // replaces that token's row with the step's own K and V. Every other
+      // block pays one scalar compare.
+      if (kc == knew && first_lane64(nt.slot) >= 0) {
+        const int r = nt.tok & (kBlock - 1);  // the token's row in the block
 #pragma unroll
-          for (int i = 0; i < Sh::kKChunks; ++i) kk[i] = ((const u32x4*)(nt.k + 8 * grp))[4 * i];
-        }
+        for (int j = 0; j < Sh::kKChunks; ++j)
+          if (kt(j) + hl / 2 == r)
+            kk[j] = *(const u32x4*)(nt.k + 64 * kl(j) + 32 * (hl % 2) + 8 * grp);
 #pragma unroll
         for (int c = 0; c < Sh::kVChunks; ++c) {
           const int idx = c * kWave + lane;
@@ -248,34 +292,55 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
     }
   };
 
+  // One block: V into the wave's LDS slice, S^T = K Q^T, lazy online
+  // softmax, O^T += V^T P^T. kFull: every token of the block is visible to
+  // every column (no masks, no zeroed rows, no -inf scores).
   auto process_block = [&](int k, const u32x4 (&kk)[Sh::kKChunks],
-                           const u32x4 (&vv)[Sh::kVChunks]) {
+                           const u32x4 (&vv)[Sh::kVChunks], auto full_tag) {
+    constexpr bool kFull = decltype(full_tag)::value;
     const int tokb = tok0 + k * tok_step;
-    // V block into this wave's LDS slice, rows past the sequence zeroed.
+    // V block into this wave's LDS slice (rows past the sequence zeroed),
+    // token t at LDS row 4*((t%8)/2) + 2*(t/8) + t%2: the transpose reads
+    // of PV then give lane group grp the tokens whose scores it holds.
 #pragma unroll
     for (int c = 0; c < Sh::kVChunks; ++c) {
       const int idx = c * kWave + lane;
       const int row = idx / (D / 8);
       const int col8 = idx % (D / 8);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *(u32x4*)(vl + row * Sh::kLdsRow + col8 * 8) = (tokb + row < tok_end) ? vv[c] : z;
+      u32x4 x = vv[c];
+      if constexpr (!kFull) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        x = (tokb + row < tok_end) ? x : z;
+      }
+      const int lrow = 4 * ((row % 8) / 2) + 2 * (row / 8) + row % 2;
+      *(u32x4*)(vl + lrow * Sh::kLdsRow + col8 * 8) = x;
     }
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // Scores: product e (valid for even rows) and o (odd rows) per group of
+    // 8 tokens; lane (hl, grp) ends with tokens 2*grp, 2*grp + 1, 8 + 2*grp,
+    // 9 + 2*grp of the block, in that order.
+    f32x4 se[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 so[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int i = 0; i < Sh::kKChunks; ++i) sacc = mfma_16x16x32(as_bf16x8(kk[i]), qv[i], sacc);
+    for (int j = 0; j < Sh::kKChunks; ++j) {
+      se[j % 2] = mfma_16x16x32(as_bf16x8(kk[j]), qv[2 * kl(j)], se[j % 2]);
+      so[j % 2] = mfma_16x16x32(as_bf16x8(kk[j]), qv[2 * kl(j) + 1], so[j % 2]);
+    }
+    const float sacc[4] = {se[0][0] + so[0][1], se[0][2] + so[0][3], se[1][0] + so[1][1],
+                           se[1][2] + so[1][3]};
     float sv[4];
-    bool over = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tok = tokb + 4 * grp + r;
-      sv[r] = (tok < tok_end && tok <= col_lim) ? sacc[r] * scale_log2 : -INFINITY;
-      over |= sv[r] > acc.m + kLazy;
+      sv[r] = sacc[r] * scale_log2;
+      if constexpr (!kFull) {
+        const int tok = tokb + 2 * grp + (r & 1) + 8 * (r >> 1);
+        sv[r] = (tok < tok_end && tok <= col_lim) ? sv[r] : -INFINITY;
+      }
     }
-    if (__any(over)) {  // wave-uniform: re-reference the softmax
-      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bm = max_across_groups(bm);
-      const float mn = fmaxf(acc.m, bm);
-      // (o and the sum are still zero while m is -inf: a column that has
+    const float bmax = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(sv[0], sv[1]), __builtin_elementwise_maximum(sv[2], sv[3]));
+    if (__any(bmax > acc.m + kLazy)) {  // wave-uniform: re-reference the softmax
+      const float mn = fmaxf(acc.m, max_across_groups(bmax));
+      // (o and the sums are still zero while m is -inf: a column that has
       // seen no visible key keeps m = -inf without a NaN)
       const float alpha = acc.m == -INFINITY ? 0.f : fast_exp2(acc.m - mn);
       acc.lsum *= alpha;
@@ -286,46 +351,93 @@ __device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      // (a column of a several-token row can meet a block with none of its
-      // keys visible before any visible one: m is still -inf there)
-      p[r] = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - acc.m);
-      acc.lsum += p[r];
+      if constexpr (kFull) {
+        p[r] = fast_exp2(sv[r] - acc.m);
+      } else {
+        // (a column of a several-token row can meet a block with none of
+        // its keys visible before any visible one: m is still -inf there)
+        p[r] = sv[r] == -INFINITY ? 0.f : fast_exp2(sv[r] - acc.m);
+      }
     }
-    const u32x2 s01 = split_pack_bf16x2(p[0], p[1]);
-    const u32x2 s23 = split_pack_bf16x2(p[2], p[3]);
-    const i16x4 phi = __builtin_bit_cast(i16x4, u32x2{s01[0], s23[0]});
-    const i16x4 plo = __builtin_bit_cast(i16x4, u32x2{s01[1], s23[1]});
     wave_lds_fence();
     // A operand V^T[d = 16*mi + hl][token 4*grp + r] by transpose reads.
     const uint16_t* vrow = vl + (4 * grp + hl / 4) * Sh::kLdsRow + 4 * (hl % 4);
+    if constexpr (kSplit) {
+      const u32x2 s01 = split_pack_bf16x2(p[0], p[1]);
+      const u32x2 s23 = split_pack_bf16x2(p[2], p[3]);
+      const i16x4 phi = __builtin_bit_cast(i16x4, u32x2{s01[0], s23[0]});
+      const i16x4 plo = __builtin_bit_cast(i16x4, u32x2{s01[1], s23[1]});
 #pragma unroll
-    for (int mi = 0; mi < Sh::kDTiles; ++mi) {
-      const i16x4 a = lds_read_tr16(vrow + 16 * mi);
-      acc.o[mi] = mfma_16x16x16(a, phi, acc.o[mi]);
-      acc.o[mi] = mfma_16x16x16(a, plo, acc.o[mi]);
+      for (int mi = 0; mi < Sh::kDTiles; ++mi) {
+        const i16x4 a = lds_read_tr16(vrow + 16 * mi);
+        acc.o[mi] = mfma_16x16x16(a, phi, acc.o[mi]);
+        acc.o[mi] = mfma_16x16x16(a, plo, acc.o[mi]);
+      }
+      acc.lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    } else {
+      // one bf16 part; the weight sum adds the same rounded values
+      const uint32_t h01 = pack_bf16x2(p[0], p[1]), h23 = pack_bf16x2(p[2], p[3]);
+      const i16x4 ph = __builtin_bit_cast(i16x4, u32x2{h01, h23});
+#pragma unroll
+      for (int mi = 0; mi < Sh::kDTiles; ++mi) {
+        const i16x4 a = lds_read_tr16(vrow + 16 * mi);
+        acc.o[mi] = mfma_16x16x16(a, ph, acc.o[mi]);
+      }
+      acc.lsum += (__uint_as_float(h01 << 16) + __uint_as_float(h01 & 0xffff0000u)) +
+                  (__uint_as_float(h23 << 16) + __uint_as_float(h23 & 0xffff0000u));
     }
     wave_lds_fence();
   };
 
-  // The main loop runs whole rounds of NBUF blocks with no early exit, so
-  // the loads still in flight at its back-edge are always the same NBUF-1
-  // ring slots in the same order and every wait is for exactly the block
-  // being consumed (an exit inside the round makes the wait at the loop head
-  // drain all loads). Block k0 + v of the last partial round sits in slot v.
+  // Blocks wholly below full_end come first (tokb grows with k): nfull of
+  // them take the unmasked path, the rest the masked one.
+  const int nfull = full_end - kBlock < tok0
+                        ? 0 : min(nk, (full_end - kBlock - tok0) / tok_step + 1);
+
+  // The ring: NBUF-1 blocks in flight ahead of the one being consumed, in
+  // whole rounds of NBUF so that every slot index is fixed at compile time
+  // and every wait is for exactly the block being consumed. The first loop
+  // takes rounds of full blocks, the second the rest (loads past the last
+  // block re-read it and go unused).
   u32x4 kb[NBUF][Sh::kKChunks], vb[NBUF][Sh::kVChunks];
 #pragma unroll
   for (int u = 0; u < NBUF - 1; ++u) load_block(u, kb[u], vb[u]);
   int k0 = 0;
-  for (; k0 + NBUF <= nk; k0 += NBUF) {
+  for (; k0 + NBUF <= nfull; k0 += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       load_block(k0 + u + NBUF - 1, kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF]);
-      process_block(k0 + u, kb[u], vb[u]);
+      process_block(k0 + u, kb[u], vb[u], std::true_type{});
     }
   }
+  for (; k0 < nk; k0 += NBUF) {
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u)
-    if (k0 + u < nk) process_block(k0 + u, kb[u], vb[u]);
+    for (int u = 0; u < NBUF; ++u) {
+      load_block(k0 + u + NBUF - 1, kb[(u + NBUF - 1) % NBUF], vb[(u + NBUF - 1) % NBUF]);
+      if (k0 + u < nk) process_block(k0 + u, kb[u], vb[u], std::false_type{});
+    }
+  }
+}
+
+// stream_blocks_impl with the weights' precision chosen per call (split_p:
+// hi + lo parts, for rows of few keys); the rest of the arguments as there.
+template <int D, int NBUF, bool kStreamV, bool kNew = false>
+__device__ __forceinline__ void stream_blocks(WaveAcc<D>& acc, const bf16x8 (&qv)[D / 32], int ids,
+                                              int nk, int tok0, int tok_step, int tok_end,
+                                              int full_end, bool split_p,
+                                              const uint16_t* __restrict__ kbase,
+                                              const uint16_t* __restrict__ vbase, int64_t kv_row,
+                                              uint16_t* vl, float scale_log2, int lane,
+                                              NewToken nt = NewToken{-1, nullptr, nullptr, -1},
+                                              int col_lim = INT32_MAX) {
+  if (split_p)  // wave-uniform
+    stream_blocks_impl<D, NBUF, kStreamV, kNew, true>(acc, qv, ids, nk, tok0, tok_step, tok_end,
+                                                      full_end, kbase, vbase, kv_row, vl,
+                                                      scale_log2, lane, nt, col_lim);
+  else
+    stream_blocks_impl<D, NBUF, kStreamV, kNew, false>(acc, qv, ids, nk, tok0, tok_step,
+                                                       tok_end, full_end, kbase, vbase, kv_row,
+                                                       vl, scale_log2, lane, nt, col_lim);
 }
 
 // Merges the states of waves that share a KV-head slot (slot = w % HG; waves
@@ -417,8 +529,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return r;
 }
 
+// Waves of an even-share workgroup: one per KV head of a head group (two
+// per head when there are four heads), at most eight.
+constexpr int kStreamMaxWaves = 8;
+
 template <int D, int NBUF, bool kStreamV>
-__global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_kernel(
+__global__ __launch_bounds__(kStreamMaxWaves * kWave) void decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ qsl,
@@ -515,17 +631,18 @@ __global__ __launch_bounds__((max_waves<D, NBUF>() * kWave)) void decode_stream_
       bf16x8 qv[Sh::kKChunks];
       load_q<D>(qv, q + ((int64_t)t0 * Hq + g * G) * D, hl, grp, ncols, G, Hq);
       const int col_lim = L - ql + min(hl, ncols - 1) / G;  // last key of the lane's column
-      const uint16_t* kbase = k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row;
+      const uint16_t* kbase = k_cache + (int64_t)g * D;
       const uint16_t* vbase = v_cache + (int64_t)g * D;
       const int32_t* trow = block_table + (int64_t)s * MB + j_lo + sub;
       for (int kc = 0; kc < nk_all; kc += kWave) {
         const int nk = min(kWave, nk_all - kc);
         const int ids = lane < nk ? trow[(int64_t)(kc + lane) * Ssub] : 0;
         stream_blocks<D, NBUF, kStreamV>(acc, qv, ids, nk, (j_lo + sub + kc * Ssub) * kBlock,
-                                         Ssub * kBlock, L, kbase, vbase, kv_row, vl, scale_log2,
-                                         lane, NewToken{-1, nullptr, nullptr, -1}, col_lim);
+                                         Ssub * kBlock, L, L - ql + 1, L <= kSplitKeys, kbase,
+                                         vbase, kv_row, vl, scale_log2, lane,
+                                         NewToken{-1, nullptr, nullptr, -1}, col_lim);
       }
-      acc.lsum = sum_across_groups(acc.lsum);
+      acc.finish();
     }
 
     const int my_slot = slot_of(p);
@@ -698,9 +815,9 @@ __global__ __launch_bounds__((max_waves<D, NBUF, kWrite>() * kWave)) void decode
     const int col_lim = L - ql + min(hl, ncols - 1) / G;  // last key of the lane's column
     stream_blocks<D, NBUF, kStreamV, kWrite>(
         acc, qv, my_blk, nmine, (b_begin + sub) * kBlock, Wsub * kBlock, tok_end,
-        k_cache + (int64_t)g * D + 8 * grp + (int64_t)hl * kv_row, v_cache + (int64_t)g * D,
-        kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt, col_lim);
-    acc.lsum = sum_across_groups(acc.lsum);
+        min(tok_end, L - ql + 1), L <= kSplitKeys, k_cache + (int64_t)g * D,
+        v_cache + (int64_t)g * D, kv_row, lds + w * Sh::kLdsWave, scale_log2, lane, nt, col_lim);
+    acc.finish();
   }
   if constexpr (kWrite) {
     if (part == nparts - 1 && sub == 0) {  // wave-uniform
@@ -972,7 +1089,8 @@ hipError_t launch_decode(const ForwardArgs& a, const DecodePlan& p, hipStream_t 
     return hipErrorInvalidValue;
   if (p.fused_combine && (p.stream || !p.counters)) return hipErrorInvalidValue;
   if (p.stream) {
-    if (p.stream_heads < 1 || p.waves % p.stream_heads || p.stream_wgs < 1 || !p.counters ||
+    if (p.waves > kStreamMaxWaves || p.stream_heads < 1 || p.waves % p.stream_heads ||
+        p.stream_wgs < 1 || !p.counters ||
         decode_stream_lds_bytes(a.head_size, p.waves, a.num_seqs) > 64 * 1024)
       return hipErrorInvalidValue;
   } else if (p.heads_per_wg < 1 || a.num_kv_heads % p.heads_per_wg ||
