@@ -197,6 +197,32 @@ def test_multi_token_decode_rows(name, hq, hkv, d, rows, hinted):
     assert_close(out.cpu()[r], want, name)
 
 
+# Decode rows around the lengths where the block loop changes path: the
+# weights' precision (hi + lo parts up to 128 keys, one bf16 part beyond),
+# the unmasked blocks (wholly inside every query column's visible range)
+# against the masked tail, and rows whose visible range ends exactly on a
+# block edge; single-token rows and rows of 2..4 query tokens.
+PATH_EDGE_ROWS = ([(1, c) for c in (111, 112, 126, 127, 128, 129, 143, 144, 255)] +
+                  [(q, c) for q in (2, 3, 4) for c in (14, 15, 16, 17, 124, 125, 126, 127, 128)])
+
+
+@pytest.mark.parametrize("schedule", ["even", "partitioned"])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (16, 4, 64)], ids=["d128", "d64"])
+def test_decode_rows_at_block_loop_path_edges(hq, hkv, d, schedule):
+    """Every row of PATH_EDGE_ROWS on the decode path (the tight
+    max_query_len hint) matches the oracle, on both schedules."""
+    spec = wl.custom(f"path_edges_{d}", hq, hkv, d, rows=PATH_EDGE_ROWS, seed=460 + d)
+    banner(f"decode path edges D{d} {schedule}: {len(PATH_EDGE_ROWS)} rows")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    out = write_and_forward(case, decode_schedule=schedule)
+    per = pa.profile_end()
+    assert "prefill" not in per and "plan" not in per, per
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, f"path edges D{d} {schedule}")
+
+
 @pytest.mark.parametrize("schedule", ["even", "partitioned"])
 @pytest.mark.parametrize("name,hq,hkv,d,rows", MULTI_TOKEN_CASES,
                          ids=[c[0] for c in MULTI_TOKEN_CASES])
