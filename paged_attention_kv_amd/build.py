@@ -75,8 +75,24 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking libpa.so failed:\n{r.stdout}\n{r.stderr}")
+    check_symbols(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def check_symbols(lib: str) -> None:
+    """Fails the build when the library leaves one of its own symbols
+    undefined (e.g. a kernel whose host launch stub the compiler did not
+    emit): such a library links but cannot be loaded."""
+    nm = shutil.which("nm")
+    if not nm:
+        return
+    r = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    own = [ln.split()[-1] for ln in r.stdout.splitlines() if "_ZN2pa" in ln]
+    if own:
+        os.remove(lib)
+        raise RuntimeError(f"libpa.so leaves {len(own)} of its own symbols undefined, e.g. "
+                           f"{own[0]}")
 
 
 if __name__ == "__main__":

@@ -59,6 +59,10 @@ __device__ __forceinline__ u32x2 split_pack_bf16x2(float a, float b) {
   return u32x2{hi, pack_bf16x2(a - ha, b - hb)};
 }
 
+// Fourth word of a raw buffer resource on gfx9-family chips: 32-bit data
+// format, so buffer loads move raw bytes.
+constexpr int kBufferWordFlags = 0x00020000;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // gfx950 LDS transpose read. Within each 16-lane block, lane i receives

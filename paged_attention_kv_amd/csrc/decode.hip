@@ -64,9 +64,6 @@ constexpr float kLazy = 8.0f;  // log2 of the largest unnormalised weight
 // Rows of at most this many keys keep the weights to about 2^-17 (bf16 hi +
 // lo parts); longer rows take one bf16 part, as the prefill tiles do.
 constexpr int kSplitKeys = 128;
-// Fourth word of a raw buffer resource on gfx9-family chips: 32-bit data
-// format, so buffer loads move raw bytes.
-constexpr int kBufferWordFlags = 0x00020000;
 // Cache-policy bit of a buffer load that marks it nontemporal (streaming).
 constexpr int kBufferNt = 2;
 

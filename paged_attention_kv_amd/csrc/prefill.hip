@@ -156,6 +156,13 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
+// 16 bytes per lane from a buffer into LDS: lane i's bytes land at lds + 16*i.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds,
+                                                int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, 0, 0, 0);
+}
+
 // Kernel modes: the two prefill tile lists, and the shared-prefix pass.
 enum TileMode { kListA = 0, kListB = 1, kPrefix = 2 };
 
@@ -304,19 +311,24 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWave
   // Tile kt straight from HBM/L2 into LDS stage `stage`: lane l of op j
   // covers row r, physical chunk pc, and fetches logical chunk pc ^ swz(r)
   // of key kt*64 + r.
+  // The loads are buffer loads into LDS from a base the wave computes per
+  // block on the scalar unit (block id * block bytes + the head's offset);
+  // the lanes' byte offsets inside the block are fixed.
+  const uint32_t blk_bytes = (uint32_t)(kBlock * kv_row * 2);
   auto dma_tile = [&](int stage, const int (&ids)[NDMA]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const int p = (j * NW + w) * 1024 + lane * 16;
       const int r = p / RB;
       const int pc = (p % RB) / 16;
-      const int64_t row = ((int64_t)ids[j] * kBlock + r % kBlock) * kv_row + (int64_t)g * D;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(k_cache + row + (pc ^ swz_k<D>(r)) * 8),
-          (__attribute__((address_space(3))) void*)(&ks[stage][(j * NW + w) * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(v_cache + row + (pc ^ swz_v<D>(r)) * 8),
-          (__attribute__((address_space(3))) void*)(&vs[stage][(j * NW + w) * 1024]), 16, 0, 0);
+      const uint64_t off = (uint64_t)(uint32_t)ids[j] * blk_bytes + (uint64_t)g * D * 2;
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)k_cache + off), (short)0, (int)blk_bytes, kBufferWordFlags);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)v_cache + off), (short)0, (int)blk_bytes, kBufferWordFlags);
+      const int rb = (int)((r % kBlock) * kv_row * 2);
+      buffer_to_lds16(kr, &ks[stage][(j * NW + w) * 1024], rb + (pc ^ swz_k<D>(r)) * 16);
+      buffer_to_lds16(vr, &vs[stage][(j * NW + w) * 1024], rb + (pc ^ swz_v<D>(r)) * 16);
     }
   };
   // Rows of tile kt at or past kv_end came from a clamped or partly used

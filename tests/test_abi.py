@@ -223,3 +223,24 @@ def test_noalloc_reports_argument_errors_like_the_workspace_call(lib):
     empty = list(args)
     empty[11] = 0       # no tokens: nothing to do, nothing launched
     assert lib.pa_write_and_forward_noalloc(*empty) == 0
+
+
+def test_build_rejects_a_library_with_its_own_symbols_undefined(tmp_path):
+    """The build's last check: a library that references one of its own
+    (namespace pa) symbols without defining it, as when the compiler drops a
+    kernel's host launch stub, is refused and removed."""
+    import shutil
+    import subprocess
+    from paged_attention_kv_amd import build
+    gxx = shutil.which("g++")
+    if not gxx or not shutil.which("nm"):
+        pytest.skip("g++ and nm are needed")
+    src = tmp_path / "u.cpp"
+    src.write_text("namespace pa { void missing(); }\nvoid use() { pa::missing(); }\n")
+    lib = tmp_path / "libu.so"
+    subprocess.run([gxx, "-shared", "-fPIC", str(src), "-o", str(lib)], check=True)
+    with pytest.raises(RuntimeError, match="undefined"):
+        build.check_symbols(str(lib))
+    assert not lib.exists()
+    # the library built in-tree passes the same check
+    build.check_symbols(pa.library_path())
