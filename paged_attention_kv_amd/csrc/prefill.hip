@@ -495,8 +495,10 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWave
     }
   }
   tile_ids(NST - 1, ids);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int stage = kt % NST;
+  // One step per tile; the loop is unrolled by NST so that every step's
+  // stage is a compile-time constant (LDS addresses become immediates).
+  auto step = [&](int kt, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int stage = decltype(stage_tag)::value;
     const int later = min(NST - 2, ntiles - 1 - kt);  // tiles issued after kt
     if (NST == 3 && later == 1) wait_loads_then_barrier<kOps>();
     else wait_loads_then_barrier<0>();
@@ -504,7 +506,7 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWave
       zero_tail(kt, stage);
       lds_writes_then_barrier();
     }
-    if (kt + NST - 1 < ntiles) dma_tile((kt + NST - 1) % NST, ids);
+    if (kt + NST - 1 < ntiles) dma_tile((stage + NST - 1) % NST, ids);
     const bool masked = (ktb + kt + 1) * BN - 1 > first_lim;
     // Tiles whose rows see at most kSplitKeys keys (SPLIT) keep P to about
     // 2^-17 (hi + lo): few weights carry each output there, and bf16
@@ -515,6 +517,13 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWave
     // kept there) and land while the next step waits for its tile.
     __builtin_amdgcn_sched_barrier(0);
     tile_ids(kt + NST, ids);
+  };
+  for (int kt = 0; kt < ntiles; kt += NST) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < ntiles) step(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NST == 3) {
+      if (kt + 2 < ntiles) step(kt + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   if constexpr (PREFIX) {
