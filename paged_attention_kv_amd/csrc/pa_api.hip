@@ -383,12 +383,21 @@ std::mutex g_side_mu;
 SideStream g_side[kMaxDevices];
 
 // The current device's side stream (g_side_mu held), or nullptr when it
-// cannot be had (the call then runs its parts one after the other).
-SideStream* side_stream_locked() {
+// cannot be had, or when the caller's stream `st` belongs to another device
+// (the call then runs its parts one after the other on `st`).
+SideStream* side_stream_locked(hipStream_t st) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
     return nullptr;
+  }
+  if (st) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    if (sdev != dev) return nullptr;
   }
   SideStream& sd = g_side[dev];
   if (!sd.s) {
@@ -541,7 +550,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
       mixed_overlap_enabled() && (int64_t)num_tokens - num_seqs >= kOverlapMinPrefillTokens &&
       !capturing(st)) {
     side_lock.lock();
-    side = side_stream_locked();
+    side = side_stream_locked(st);
     if (!side) side_lock.unlock();
   }
   // The planner runs on the caller's stream (one workgroup: beside the
