@@ -201,7 +201,8 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
  * (160 of them, PA_MIXED_DECODE_WGS overrides) run on `stream` and leave
  * CUs to the prefill tiles. Work enqueued on `stream` after the call still
  * sees all of its results. Calls made while `stream` is being captured
- * into a graph, calls with PA_FORWARD_SERIAL, pa_write_and_forward_noalloc
+ * into a graph, calls whose `stream` belongs to a device other than the
+ * current one, calls with PA_FORWARD_SERIAL, pa_write_and_forward_noalloc
  * and every process with PA_MIXED_OVERLAP=0 keep all launches on `stream`.
  */
 #define PA_FORWARD_SHARED_BLOCKS 1u
