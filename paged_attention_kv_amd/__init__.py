@@ -146,11 +146,23 @@ def _check(status: int) -> None:
         raise PaError(status, last_error())
 
 
+# torch's raw-stream query (one C call) where this torch has it; the public
+# current_stream() builds a Stream object on every call (~2 us).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor):
+    """The HIP stream torch has current for t's device (t is on a device)."""
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _dev_tensor(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int) -> None:
+    # the usual case in one pass; the checks below name what is wrong
+    if (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype is dtype and t.dim() == ndim
+            and t.is_contiguous()):
+        return
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -207,22 +219,39 @@ _workspaces: dict = {}
 _retired_workspaces: list = []
 
 
-def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    key = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        if torch.cuda.is_current_stream_capturing():
-            raise RuntimeError(
-                "the implicit workspace would have to grow during graph capture: pass a "
-                "workspace (forward_workspace_bytes(...) bytes, its first "
-                "WORKSPACE_COUNTER_BYTES zero) to calls made under capture")
-        # zero-filled once: the leading counter region must start at zero
-        # (every call leaves it zero)
-        if ws is not None:
-            _retired_workspaces.append(ws)
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+def _workspace(device: int, nbytes: int) -> torch.Tensor:
+    """The implicit workspace of device index ``device``, grown to nbytes."""
+    ws = _workspaces.get(device)
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError(
+            "the implicit workspace would have to grow during graph capture: pass a "
+            "workspace (forward_workspace_bytes(...) bytes, its first "
+            "WORKSPACE_COUNTER_BYTES zero) to calls made under capture")
+    # zero-filled once: the leading counter region must start at zero
+    # (every call leaves it zero)
+    if ws is not None:
+        _retired_workspaces.append(ws)
+    ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=torch.device("cuda", device))
+    _workspaces[device] = ws
     return ws
+
+
+_need_cache: dict = {}
+
+
+def _workspace_need(*sizes) -> int:
+    """pa_forward_workspace_bytes of these sizes (T, S, Hq, Hkv, D, MB, max
+    query length, max sequence length hints), remembered per size tuple: the
+    library's answer depends on nothing else."""
+    n = _need_cache.get(sizes)
+    if n is None:
+        n = int(load_library().pa_forward_workspace_bytes(*sizes))
+        if len(_need_cache) > 4096:
+            _need_cache.clear()
+        _need_cache[sizes] = n
+    return n
 
 
 def _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, out,
@@ -257,11 +286,11 @@ def _forward_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, s
         if decode_schedule not in _SCHEDULE_FLAGS:
             raise ValueError(f"decode_schedule must be one of {sorted(_SCHEDULE_FLAGS)}")
         flags |= _SCHEDULE_FLAGS[decode_schedule]
-    need = lib.pa_forward_workspace_bytes(T, S, Hq, Hkv, D, MB, max_query_len or 0,
-                                          max_seq_len or 0)
     if workspace is None:
-        workspace = _workspace(q.device, need)
-    elif workspace.device != q.device:
+        workspace = _workspace(q.get_device(), _workspace_need(T, S, Hq, Hkv, D, MB,
+                                                               max_query_len or 0,
+                                                               max_seq_len or 0))
+    elif not workspace.is_cuda or workspace.get_device() != q.get_device():
         raise ValueError("workspace must be on q's device")
     tail = (block_table.data_ptr(), seq_lens.data_ptr(), query_start_loc.data_ptr(), float(scale),
             out.data_ptr(), T, S, Hq, Hkv, D, bs, MB, NB, max_query_len or 0, max_seq_len or 0,
@@ -335,8 +364,8 @@ def forward_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     if need == 0:
         raise ValueError("unsupported sizes for pa_forward_shared_prefix")
     if workspace is None:
-        workspace = _workspace(q.device, need)
-    elif workspace.device != q.device:
+        workspace = _workspace(q.get_device(), need)
+    elif not workspace.is_cuda or workspace.get_device() != q.get_device():
         raise ValueError("workspace must be on q's device")
     _check(lib.pa_forward_shared_prefix(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
