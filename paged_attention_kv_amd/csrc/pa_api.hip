@@ -124,14 +124,25 @@ int32_t choose_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t waves
 }
 
 // Partitioned decode with the merge in the kernel: the last workgroup of a
-// split row merges its partials, so no combine launch follows.
-// PA_DECODE_FUSED_COMBINE=0 turns it off (for comparisons). Splitting rows
-// further for balance on this path measured slower on the decode workloads
-// (the split adds workgroups and hand-overs while HBM is already the
-// limit), so partitions keep the sizes chosen above.
-bool decode_fused_combine(int32_t num_seqs, int32_t num_kv_heads) {
-  static const int v = env_int("PA_DECODE_FUSED_COMBINE", 0, 1, 1);
-  return v == 1 && (int64_t)num_seqs * num_kv_heads <= kCounterSlots;
+// split row merges its partials, so no combine launch follows. Each
+// workgroup that hands a partial over pays an agent-scope release (an L2
+// write-back); with partitions of more than kFusedMergeMaxPartTokens keys
+// that measured 4-40% slower than leaving the merge to the combine launch
+// (2 partitions of 1500 keys at 48 x 4 (row, KV head): 43.3 against
+// 31.1 us), with partitions of up to 1024 keys faster (64 of 128 keys at
+// 1 x 4: 15.4 against 17.7 us). PA_DECODE_FUSED_COMBINE=0 turns the
+// in-kernel merge off, =2 uses it at every partition length (comparisons).
+// Splitting rows further for balance on this path measured slower on the
+// decode workloads (the split adds workgroups and hand-overs while HBM is
+// already the limit), so partitions keep the sizes chosen above.
+constexpr int32_t kFusedMergeMaxPartTokens = 1024;
+bool decode_counters_fit(int32_t num_seqs, int32_t num_kv_heads) {
+  return (int64_t)num_seqs * num_kv_heads <= kCounterSlots;
+}
+bool decode_fused_combine(int32_t num_seqs, int32_t num_kv_heads, int32_t part_tokens) {
+  static const int v = env_int("PA_DECODE_FUSED_COMBINE", 0, 2, 1);
+  return v != 0 && decode_counters_fit(num_seqs, num_kv_heads) &&
+         (v == 2 || part_tokens <= kFusedMergeMaxPartTokens);
 }
 
 bool supported_group(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
@@ -222,8 +233,8 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   w.stream_waves = kStreamWaves / w.stream_heads * w.stream_heads;
   w.stream_wgs = decode_stream_wgs();
   w.waves = decode_waves(head_size, w.prefetch);
-  w.fused_combine = decode_fused_combine(num_seqs, num_kv_heads);
   w.part_tokens = choose_part_tokens(num_seqs, num_kv_heads, w.waves, max_len);
+  w.fused_combine = decode_fused_combine(num_seqs, num_kv_heads, w.part_tokens);
   w.num_parts_max = (max_len + w.part_tokens - 1) / w.part_tokens;
   if (w.num_parts_max > kMaxGridZ) return false;
   const size_t stream_rows = w.stream_ok ? (size_t)w.stream_wgs * 2 * w.qmax * num_q_heads : 0;
@@ -873,7 +884,7 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   // partials with its own row's (no combine launch), through the counters at
   // the start of the workspace.
   dp.counters = (int32_t*)ws;
-  dp.fused_combine = decode_fused_combine(num_seqs, num_kv_heads);
+  dp.fused_combine = decode_fused_combine(num_seqs, num_kv_heads, pl.part_tokens);
   e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix decode launch");
   return PA_OK;

@@ -492,6 +492,30 @@ def test_shared_prefix_combine_launch_for_many_rows():
     assert_close(out.cpu()[r], want, spec.name)
 
 
+# Small batches split their rows into partitions. Partitions of up to 1024
+# keys are merged in the decode kernel by each row's last workgroup; longer
+# ones by the combine launch. 24 rows x 8 KV heads of 1651..2501 keys: two
+# partitions of 1264 keys, every row split; 6 rows x 8 KV heads: six
+# partitions of 432 keys.
+MERGE_PATH_CASES = [("long_parts", 24, 1), ("short_parts", 6, 0)]
+
+
+@pytest.mark.parametrize("name,nrows,combines", MERGE_PATH_CASES,
+                         ids=[c[0] for c in MERGE_PATH_CASES])
+def test_split_rows_merge_path_by_partition_length(name, nrows, combines):
+    rows = [(1, 2500 - 37 * i) for i in range(nrows)]
+    spec = wl.custom(name, 32, 8, 128, rows=rows, seed=220 + nrows)
+    banner(f"split rows, {name}: S={spec.num_seqs} Hkv=8 D=128")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    out = write_and_forward(case, decode_schedule="partitioned")
+    per = pa.profile_end()
+    assert per["decode"][0] == 1 and per.get("combine", (0,))[0] == combines, per
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, spec.name)
+
+
 # ---------------------------------------------------------------------------
 # Write and forward in one call
 # ---------------------------------------------------------------------------
