@@ -148,7 +148,10 @@ class StepInputs:
                           shared_blocks=spec.shared_prefix_blocks > 0)
 
 
-FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan", "prefix")
+# (write_plan: the KV write and the tile planner in one launch, counted with
+# the planner)
+FORWARD_KERNELS = ("decode", "combine", "prefill", "prefill_short", "plan", "prefix",
+                   "write_plan")
 
 
 def percentile(xs, f):

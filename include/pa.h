@@ -392,6 +392,7 @@ int pa_probe_block_read(const void* k_cache, const void* v_cache, const int32_t*
 #define PA_KERNEL_PREFILL_SHORT 4 /* prefill tiles seeing few keys             */
 #define PA_KERNEL_PLAN 5          /* prefill tile planner                      */
 #define PA_KERNEL_PREFIX 6        /* shared-prefix pass (pa_forward_shared_prefix) */
+#define PA_KERNEL_WRITE_PLAN 7    /* KV write + tile planner in one launch     */
 #define PA_KERNEL_CLASSES 8
 
 typedef struct pa_profile {

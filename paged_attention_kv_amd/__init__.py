@@ -98,7 +98,7 @@ SIGNATURES = {
 
 # Kernel classes of the timing facility (PA_KERNEL_* in include/pa.h).
 KERNEL_CLASSES = {0: "cache_write", 1: "decode", 2: "combine", 3: "prefill",
-                  4: "prefill_short", 5: "plan", 6: "prefix"}
+                  4: "prefill_short", 5: "plan", 6: "prefix", 7: "write_plan"}
 _NCLASS = 8
 
 

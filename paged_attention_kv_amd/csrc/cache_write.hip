@@ -16,16 +16,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(
     const int64_t* __restrict__ slot_mapping, u32x4* __restrict__ k_cache,
     u32x4* __restrict__ v_cache, int64_t total_chunks, int32_t chunks_per_token) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total_chunks) return;
-  const int64_t t = i / chunks_per_token;
-  const int32_t c = (int32_t)(i - t * chunks_per_token);
-  const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;  // padding token
-  const int64_t dst = slot * chunks_per_token + c;
-  const u32x4 kv = __builtin_nontemporal_load(k + i);
-  const u32x4 vv = __builtin_nontemporal_load(v + i);
-  k_cache[dst] = kv;
-  v_cache[dst] = vv;
+  if (i < total_chunks) write_kv_chunk(k, v, slot_mapping, k_cache, v_cache, i, chunks_per_token);
 }
 
 hipError_t launch_cache_write(const void* k, const void* v, const int64_t* slot_mapping,

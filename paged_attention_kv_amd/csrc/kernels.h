@@ -98,6 +98,10 @@ struct PrefillPlan {
 // The planner (one workgroup), then the tiles it listed; the tiles may go to
 // another stream ordered after the planner.
 hipError_t launch_prefill_plan(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
+// The KV write of a.num_tokens tokens and the planner in one launch.
+hipError_t launch_write_and_plan(const ForwardArgs& a, const PrefillPlan& p, const void* k,
+                                 const void* v, const int64_t* slot_mapping, void* k_cache,
+                                 void* v_cache, hipStream_t stream);
 hipError_t launch_prefill_tiles(const ForwardArgs& a, const PrefillPlan& p, hipStream_t stream);
 // Query tokens per prefill tile for a given group size (MFMA rows / G), for
 // tiles whose rows see many keys (list A) and few (list B).
@@ -107,6 +111,9 @@ int32_t prefill_split_tile_queries(int32_t group);
 int32_t prefix_tile_rows(int32_t group);
 // Upper bound on list-B tiles per row.
 int32_t prefill_split_tiles_per_row(int32_t group);
+// Tiles whose rows see more keys than this go to list A (none can when no
+// row is longer).
+int32_t prefill_split_keys();
 
 // Shared-prefix pass: the first prefix_keys keys of every decode row come
 // from the same blocks (row 0's table); chunks of chunk_keys keys are

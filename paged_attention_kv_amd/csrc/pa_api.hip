@@ -543,11 +543,6 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   dp.qmax = w.qmax;
   const bool fused = wr && max_query_len_hint == 1 && !dp.stream &&
                      w.waves <= pa::decode_max_waves(head_size, w.prefetch, true);
-  if (wr && !fused) {
-    hipError_t e = pa::launch_cache_write(wr->k, wr->v, wr->slot_mapping, wr->k_cache,
-                                          wr->v_cache, num_tokens, num_kv_heads, head_size, st);
-    if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward cache write launch");
-  }
 
   // A mixed batch on even shares with enough prefill tokens (num_tokens -
   // num_seqs of them at least) runs its prefill tiles on the side stream,
@@ -564,8 +559,10 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     side = side_stream_locked(st);
     if (!side) side_lock.unlock();
   }
-  // The planner runs on the caller's stream (one workgroup: beside the
-  // decode launch it would wait behind the decode's loads), then the fork.
+  // The new tokens' write (unless the decode launch makes it) and the
+  // planner run on the caller's stream (the planner is one workgroup: beside
+  // the decode launch it would wait behind the decode's loads), in one
+  // launch when both are needed; then the fork.
   pa::PrefillPlan pp{};
   if (has_prefill) {
     pp.tile_queries = w.tile_queries;
@@ -579,8 +576,23 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     pp.tiles_a = (int32_t*)(ws + w.off_tiles_a);
     pp.tiles_b = (int32_t*)(ws + w.off_tiles_b);
     pp.counts = (int32_t*)(ws + w.off_counts);
-    hipError_t e = pa::launch_prefill_plan(a, pp, st);
-    if (e != hipSuccess) return hip_fail(e, "pa_forward prefill planner launch");
+    // no tile sees more keys than the longest row has: list A stays empty
+    if (a.max_seq_len <= pa::prefill_split_keys()) pp.bound_a = 0;
+  }
+  if (wr && !fused && has_prefill) {
+    hipError_t e = pa::launch_write_and_plan(a, pp, wr->k, wr->v, wr->slot_mapping, wr->k_cache,
+                                             wr->v_cache, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward write and planner launch");
+  } else {
+    if (wr && !fused) {
+      hipError_t e = pa::launch_cache_write(wr->k, wr->v, wr->slot_mapping, wr->k_cache,
+                                            wr->v_cache, num_tokens, num_kv_heads, head_size, st);
+      if (e != hipSuccess) return hip_fail(e, "pa_write_and_forward cache write launch");
+    }
+    if (has_prefill) {
+      hipError_t e = pa::launch_prefill_plan(a, pp, st);
+      if (e != hipSuccess) return hip_fail(e, "pa_forward prefill planner launch");
+    }
   }
   hipStream_t pst = st;  // the prefill tiles' stream
   if (side) {

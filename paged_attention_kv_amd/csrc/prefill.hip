@@ -59,7 +59,8 @@ constexpr int kPlanThreads = 1024;
 // list A holds tiles whose rows see more than kSplitKeys keys, each row's
 // heaviest (latest) tiles first; list B the tiles that see at most
 // kSplitKeys keys (they keep P as bf16 hi + lo).
-__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+// (one workgroup of kPlanThreads threads builds both lists)
+__device__ __forceinline__ void plan_tiles(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
     int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
     int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts) {
@@ -128,6 +129,34 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     tiles_b[2 * i] = -1;
     tiles_b[2 * i + 1] = -1;
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
+    int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
+    int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts) {
+  plan_tiles(qsl, seq_lens, S, bq_a, bq_b, tiles_a, bound_a, tiles_b, bound_b, counts);
+}
+
+// The KV write and the planner in one launch (pa_write_and_forward on a
+// batch with prefill rows; one kernel boundary fewer per step): workgroup 0
+// plans the tiles, the others write the new tokens, one 16-byte chunk of K
+// and of V per thread. The tiles, which read the new tokens through the
+// caches, start after this launch has ended, as they did after the two it
+// replaces.
+__global__ __launch_bounds__(kPlanThreads) void write_plan_kernel(
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
+    int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
+    int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts,
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int64_t* __restrict__ slot_mapping, u32x4* __restrict__ k_cache,
+    u32x4* __restrict__ v_cache, int64_t total_chunks, int32_t chunks_per_token) {
+  if (blockIdx.x == 0) {  // workgroup-uniform
+    plan_tiles(qsl, seq_lens, S, bq_a, bq_b, tiles_a, bound_a, tiles_b, bound_b, counts);
+    return;
+  }
+  const int64_t i = (int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
+  if (i < total_chunks) write_kv_chunk(k, v, slot_mapping, k_cache, v_cache, i, chunks_per_token);
 }
 
 // Waits until at most N vector-memory operations of this wave are in flight
@@ -688,6 +717,8 @@ int32_t prefill_tile_queries(int32_t group) { return 16 * kRowTilesA * kWavesA /
 int32_t prefill_split_tile_queries(int32_t group) { return 16 * kRowTiles * kWavesB / group; }
 int32_t prefix_tile_rows(int32_t group) { return 16 * kRowTiles * kWavesP / group; }
 
+int32_t prefill_split_keys() { return kSplitKeys; }
+
 int32_t prefill_split_tiles_per_row(int32_t group) {
   const int32_t bq = 16 * kRowTiles * kWavesB / group;
   return (kSplitKeys + bq - 1) / bq;
@@ -701,6 +732,26 @@ hipError_t launch_prefill_plan(const ForwardArgs& a, const PrefillPlan& p, hipSt
                      p.split_tile_queries, p.tiles_a,
                      p.bound_a, p.tiles_b, p.bound_b, p.counts);
   profile_end(PA_KERNEL_PLAN, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_and_plan(const ForwardArgs& a, const PrefillPlan& p, const void* k,
+                                 const void* v, const int64_t* slot_mapping, void* k_cache,
+                                 void* v_cache, hipStream_t stream) {
+  if (p.bound_a <= 0 && p.bound_b <= 0)
+    return launch_cache_write(k, v, slot_mapping, k_cache, v_cache, a.num_tokens,
+                              a.num_kv_heads, a.head_size, stream);
+  const int32_t chunks_per_token = a.num_kv_heads * a.head_size / 8;
+  const int64_t total = (int64_t)a.num_tokens * chunks_per_token;
+  const int64_t blocks = 1 + (total + kPlanThreads - 1) / kPlanThreads;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  profile_begin(PA_KERNEL_WRITE_PLAN, stream);
+  hipLaunchKernelGGL(write_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), 0, stream,
+                     a.query_start_loc, a.seq_lens, a.num_seqs, p.tile_queries,
+                     p.split_tile_queries, p.tiles_a, p.bound_a, p.tiles_b, p.bound_b, p.counts,
+                     (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
+                     (u32x4*)v_cache, total, chunks_per_token);
+  profile_end(PA_KERNEL_WRITE_PLAN, stream);
   return hipGetLastError();
 }
 

@@ -596,7 +596,9 @@ def test_write_and_forward_skips_negative_slots():
     assert_close(out.cpu()[r], want, "rows with slots")
 
 
-def test_write_and_forward_mixed_batch_falls_back_to_two_launches():
+def test_write_and_forward_mixed_batch_writes_before_its_tiles():
+    """A mixed batch: the write and the tile planner share one launch, then
+    the tiles (list A and list B) and the decode launch."""
     rows = [(1, 900), (37, 100), (1, 33), (200, 200), (1, 5000)]
     spec = wl.custom("mixed_fused", 32, 8, 128, rows=rows, seed=92)
     case = wl.make_case(spec, device=DEV)
@@ -604,9 +606,34 @@ def test_write_and_forward_mixed_batch_falls_back_to_two_launches():
     pa.profile_begin()
     out = fused_call(case, max_query_len=200)
     per = pa.profile_end()
-    assert per["cache_write"][0] == 1 and per["prefill"][0] == 1 and per["decode"][0] == 1
+    assert per["write_plan"][0] == 1 and per["prefill"][0] == 1 and per["decode"][0] == 1, per
+    assert per["prefill_short"][0] == 1 and "cache_write" not in per and "plan" not in per, per
     r, want = view.expect()
     assert_close(out.cpu()[r], want, "mixed")
+
+
+@pytest.mark.parametrize("hinted", [True, False])
+def test_short_rows_launch_no_long_tile_list(hinted):
+    """No row longer than 128 keys (by the hint, or by the table's width when
+    there is none): no tile can see more, so list A is not launched; the
+    rows' tiles all run from list B."""
+    rows = [(40, 20), (1, 50), (7, 0), (100, 27), (1, 3)]
+    spec = wl.custom("short_rows", 32, 8, 128, rows=rows, seed=93, max_blocks_per_seq=8)
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    if hinted:
+        out = fused_call(case, max_query_len=100)
+    else:
+        out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
+                                   case.q, case.block_table, case.seq_lens,
+                                   case.query_start_loc, case.scale)
+        torch.cuda.synchronize()
+    per = pa.profile_end()
+    assert "prefill" not in per and per["prefill_short"][0] == 1, per
+    assert per["write_plan"][0] == 1 and per["decode"][0] == 1, per
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, "short rows")
 
 
 def test_nan_poison_outside_context_does_not_leak():
