@@ -139,6 +139,43 @@ def test_mixed_workload_rows(schedule):
     assert_close(out[rows], want, f"mixed/prefill rows (chunk {full - 256} whole)")
 
 
+def test_mixed_workload_through_write_and_forward():
+    """Workload 3 as the benchmark times it: one pa_write_and_forward call
+    with the benchmark's hints (the write and the tile planner in one
+    launch, the prefill tiles beside the decode on the library's second
+    stream). Every decode row, one whole chunk and the edge and sampled rows
+    of the others against the oracle; the written blocks bit-exact against
+    ref_cache_write and every other block of the pool unchanged."""
+    spec = wl.config(3)
+    banner("workload 3 through pa_write_and_forward (write with planner, overlap)")
+    case = wl.make_case(spec, device=DEV)
+    chunks = list(range(256, 260))
+    full = max(chunks, key=lambda s: spec.ctx_lens[s])
+    edge = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 127, 128, 1023, 1024, 1982, 1983]
+    per = {s: (range(1984) if s == full else
+               sorted(set(edge + random.Random(s + 7).sample(range(1984), 64)))) for s in chunks}
+    dec_view = OracleView(case, range(256))
+    pre_view = OracleView(case, chunks)
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    pa.profile_begin()
+    out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
+                               case.q, case.block_table, case.seq_lens, case.query_start_loc,
+                               case.scale, max_query_len=max(spec.q_lens),
+                               max_seq_len=max(spec.seq_lens))
+    torch.cuda.synchronize()
+    launches = pa.profile_end()
+    assert launches["write_plan"][0] == 1 and "cache_write" not in launches, launches
+    assert launches["prefill"][0] == 1 and launches["decode"][0] == 1, launches
+    assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
+    del k0, v0
+    out = out.cpu()
+    rows, want = dec_view.expect()
+    assert_close(out[rows], want, "mixed, one call/all 256 decode rows")
+    del dec_view
+    rows, want = pre_view.expect(per)
+    assert_close(out[rows], want, f"mixed, one call/prefill rows (chunk {full - 256} whole)")
+
+
 @pytest.mark.parametrize("schedule", [None, "partitioned"])
 def test_long_decode_all_rows(schedule):
     spec = wl.config(4)
@@ -610,6 +647,36 @@ def test_write_and_forward_mixed_batch_writes_before_its_tiles():
     assert per["prefill_short"][0] == 1 and "cache_write" not in per and "plan" not in per, per
     r, want = view.expect()
     assert_close(out.cpu()[r], want, "mixed")
+
+
+def test_write_and_forward_mixed_batch_skips_negative_slots():
+    """A mixed batch whose decode and prefill rows both hold tokens with
+    slot < 0: the write with the planner in one launch leaves the pool and
+    the output bit-identical to the two-call sequence (cache write, then
+    forward), and the rows whose tokens all have slots match the oracle."""
+    rows = [(1, 900), (37, 100), (1, 33), (200, 200), (1, 5000), (9, 0)]
+    spec = wl.custom("neg_mixed", 32, 8, 128, rows=rows, seed=94)
+    case = wl.make_case(spec, device=DEV)
+    slots = case.slot_mapping.clone()
+    qsl = case.query_start_loc.cpu().tolist()
+    slots[qsl[2]] = -1            # the decode row 2's token
+    slots[qsl[3] + 150] = -3      # a token inside the 200-token chunk
+    case.slot_mapping = slots
+    view = OracleView(case, [0, 1, 4, 5])
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    pa.profile_begin()
+    one = fused_call(case, max_query_len=200).clone()
+    launches = pa.profile_end()
+    assert launches["write_plan"][0] == 1, launches
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    case.k_cache.copy_(k0)
+    case.v_cache.copy_(v0)
+    two = write_and_forward(case)
+    assert torch.equal(kc.view(torch.int16), case.k_cache.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), case.v_cache.view(torch.int16))
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    r, want = view.expect()
+    assert_close(one.cpu()[r], want, "mixed rows with slots")
 
 
 @pytest.mark.parametrize("hinted", [True, False])
