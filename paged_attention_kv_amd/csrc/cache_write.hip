@@ -6,6 +6,7 @@
 // and in the cache row, so the copy is a run of 16-byte moves per token.
 #include "common.h"
 #include "kernels.h"
+#include "kv_write.h"
 
 namespace pa {
 

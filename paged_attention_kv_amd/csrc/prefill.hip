@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "kv_write.h"
 
 namespace pa {
 
