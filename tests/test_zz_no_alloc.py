@@ -17,11 +17,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 # (name, Hq, Hkv, D, rows): the first batch uses the scratch array's counter
-# region (long decode rows split between workgroups and merged in the kernel),
-# its partials and the prefill tile lists; the second is smaller, decode rows
-# only (the write rides in the decode launch).
+# region (long decode rows split into partitions of 1008 keys, short enough
+# to be merged in the kernel), its partials and the prefill tile lists; the
+# second is smaller, decode rows only (the write rides in the decode launch).
 CALLS = [
-    ("mixed_larger", 32, 8, 128, [(1, 9000), (1, 300), (40, 100), (1, 4100), (200, 0),
+    ("mixed_larger", 32, 8, 128, [(1, 4000), (1, 300), (40, 100), (1, 3100), (200, 0),
                                   (1, 17), (3, 60), (1, 2500)]),
     ("decode_smaller", 32, 8, 128, [(1, 50), (1, 2000), (1, 1), (1, 777)]),
 ]
@@ -37,9 +37,12 @@ def run(spec, noalloc):
     if noalloc:
         torch.cuda.synchronize()
         before = torch.cuda.memory_allocated()
+        pa.profile_begin()
         pa.write_and_forward_noalloc(*args, out=out, **hints)
         torch.cuda.synchronize()
+        launches = pa.profile_end()
         assert torch.cuda.memory_allocated() == before
+        assert "combine" not in launches, launches  # split rows merged in the kernel
     else:
         ws = torch.zeros(pa.forward_workspace_bytes(spec.num_tokens, spec.num_seqs,
                                                     spec.num_q_heads, spec.num_kv_heads,
