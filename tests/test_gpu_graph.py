@@ -5,7 +5,7 @@ eager call on the same inputs, and matches the oracle on them (whose inputs
 are a CPU copy of the rows' blocks taken before the library was called, the
 replay's own q, k and v written into it by the oracle). Covers the fused
 decode launch, partitioned rows merged in the kernel (arrival counters, reset by the kernels
-themselves, so replays start from zero), the even-share schedule, a mixed
+themselves, so replays start from zero) or by the combine launch, the even-share schedule, a mixed
 step with prefill tiles and their device planner, rows of four query tokens
 on both decode schedules, the shared-prefix pass, and several steps
 in one graph."""
@@ -24,7 +24,10 @@ DEV = "cuda:0"
 CASES = [
     # name, Hq, Hkv, D, rows, schedule
     ("decode_fused", 32, 4, 64, [(1, 512 + 37 * i) for i in range(64)], "partitioned"),
-    ("decode_long_rows", 64, 8, 128, [(1, 30000), (1, 12000), (1, 5)], "partitioned"),
+    # rows split into partitions of 736 keys (merged in the kernel) and of
+    # 2736 keys (merged by the combine launch)
+    ("decode_long_rows", 64, 8, 128, [(1, 8000), (1, 3000), (1, 5)], "partitioned"),
+    ("decode_long_rows_combine", 64, 8, 128, [(1, 30000), (1, 12000), (1, 5)], "partitioned"),
     ("even_shares", 32, 8, 128, [(1, 2000 + 61 * i) for i in range(200)], "even"),
     ("mixed", 32, 8, 128, [(1, 900), (300, 1000), (1, 33), (64, 0), (1, 4000)], None),
     # rows of four query tokens (speculative verify) on each decode schedule
