@@ -429,6 +429,30 @@ def test_sweep_full_oracle(d, hq, hkv):
     assert_close(out.cpu()[r], want, spec.name)
 
 
+# The longest rows here: 131072 keys (8192 table entries) in one row, as a
+# decode row on every schedule (beside a short one), and as a 64-token chunk
+# at the end of that context (first, middle and last query rows checked).
+@pytest.mark.parametrize("schedule", [None, "even", "partitioned"])
+def test_longest_decode_row(schedule):
+    spec = wl.custom("longest", 32, 8, 128, rows=[(1, 131071), (1, 17)], seed=97)
+    banner(f"decode row of 131072 keys, schedule {schedule}")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    out = write_and_forward(case, decode_schedule=schedule)
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, f"longest decode ({schedule})")
+
+
+def test_longest_chunk():
+    spec = wl.custom("longest_chunk", 32, 8, 128, rows=[(64, 131008)], seed=98)
+    banner("64-token chunk after 131008 keys")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [0])
+    out = write_and_forward(case)
+    r, want = view.expect({0: [0, 31, 63]})
+    assert_close(out.cpu()[r], want, "longest chunk")
+
+
 @pytest.mark.parametrize("part", [None])
 def test_long_context_split_into_many_partitions(part):
     rows = [(1, 5000), (1, 17), (1, 2048), (1, 2049), (3, 4000), (1, 1023)]
