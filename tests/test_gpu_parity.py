@@ -443,6 +443,21 @@ def test_longest_decode_row(schedule):
     assert_close(out.cpu()[r], want, f"longest decode ({schedule})")
 
 
+def test_long_prompt_from_an_empty_context():
+    """One 8192-token prompt with no cached context (causal over itself):
+    rows at and around every 128-row tile edge of the first and last tiles,
+    and samples in between."""
+    spec = wl.custom("prompt8k", 32, 8, 128, rows=[(8192, 0)], seed=99)
+    banner("8192-token prompt, empty context")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [0])
+    out = write_and_forward(case)
+    pick = sorted(set([0, 1, 63, 64, 127, 128, 129, 255, 256, 4095, 4096, 8063, 8064,
+                       8190, 8191] + random.Random(5).sample(range(8192), 24)))
+    r, want = view.expect({0: pick})
+    assert_close(out.cpu()[r], want, "8192-token prompt")
+
+
 def test_longest_chunk():
     spec = wl.custom("longest_chunk", 32, 8, 128, rows=[(64, 131008)], seed=98)
     banner("64-token chunk after 131008 keys")
