@@ -893,8 +893,11 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
   dp.part_base = pl.chunks;
   dp.qmax = 1;
   // The last workgroup of each (row, KV head) merges the prefix chunks'
-  // partials with its own row's (no combine launch), through the counters at
-  // the start of the workspace.
+  // partials with its own row's, through the counters at the start of the
+  // workspace (a row whose own keys fit one partition merges them directly);
+  // rows whose own keys are split into partitions longer than the in-kernel
+  // merge takes (decode_fused_combine) leave every partial to the combine
+  // launch.
   dp.counters = (int32_t*)ws;
   dp.fused_combine = decode_fused_combine(num_seqs, num_kv_heads, pl.part_tokens);
   e = pa::launch_decode(a, dp, st);
