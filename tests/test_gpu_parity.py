@@ -359,6 +359,10 @@ SHARED_PREFIX_CASES = [
     # 16 KV heads: all of a row's heads in one workgroup at D = 64, eight at D = 128
     ("h16_d64", 16, 16, 64, 9, [2, 31, 600, 1]),
     ("h16_d128", 32, 16, 128, 9, [2, 31, 600, 1]),
+    # long own parts on 128 rows: up to four partitions of 1024 keys per
+    # row, handed over through the arrival counters and merged with the
+    # chunks' partials by the row's last workgroup
+    ("long_own", 32, 8, 128, 4, [4000 - 13 * i for i in range(128)]),
 ]
 
 
