@@ -177,9 +177,15 @@ def test_shared_prefix_workspace(lib):
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define PA_BLOCK_SIZE (\d+)", text).group(1)) == pa.BLOCK_SIZE
-    for name in ("SHARED_BLOCKS", "DECODE_EVEN_SHARES", "DECODE_PARTITIONED"):
+    for name in ("SHARED_BLOCKS", "DECODE_EVEN_SHARES", "DECODE_PARTITIONED", "SERIAL"):
         assert int(re.search(rf"#define PA_FORWARD_{name} (\d+)u", text).group(1)) == \
             getattr(pa, "FORWARD_" + name)
+    # kernel classes of the timing interface: the binding names every one
+    classes = {int(v): k.lower() for k, v in re.findall(r"#define PA_KERNEL_(\w+) (\d+)", text)
+               if k != "CLASSES"}
+    assert classes == pa.KERNEL_CLASSES
+    n = int(re.search(r"#define PA_KERNEL_CLASSES (\d+)", text).group(1))
+    assert max(classes) < n
     m = re.search(r"#define PA_WORKSPACE_COUNTER_BYTES \((\d+)u \* (\d+)u\)", text)
     assert int(m.group(1)) * int(m.group(2)) == pa.WORKSPACE_COUNTER_BYTES
 
