@@ -610,8 +610,14 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     if (e != hipSuccess && rc == PA_OK) return hip_fail(e, "pa_forward: joining the prefill stream");
     return rc;
   };
+  // With the side stream, its prefill tiles are the longer of the two
+  // parts: the short list (tiles that see few keys) follows the decode on
+  // the caller's stream instead of the long list on the side stream.
+  pa::PrefillPlan pp_side = pp, pp_after = pp;
+  if (side) pp_side.bound_b = 0;
+  pp_after.bound_a = 0;
   if (has_prefill) {
-    hipError_t e = pa::launch_prefill_tiles(a, pp, pst);
+    hipError_t e = pa::launch_prefill_tiles(a, pp_side, pst);
     if (e != hipSuccess) return join(hip_fail(e, "pa_forward prefill launch"));
   }
   dp.stream_wgs = side ? std::min(w.stream_wgs, mixed_decode_wgs()) : w.stream_wgs;
@@ -636,6 +642,10 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   dp.v_cache_w = fused ? wr->v_cache : nullptr;
   hipError_t e = pa::launch_decode(a, dp, st);
   if (e != hipSuccess) return join(hip_fail(e, "pa_forward decode launch"));
+  if (has_prefill && side) {
+    e = pa::launch_prefill_tiles(a, pp_after, st);
+    if (e != hipSuccess) return join(hip_fail(e, "pa_forward prefill launch"));
+  }
   return join(PA_OK);
 }
 
