@@ -194,12 +194,13 @@ int pa_forward(const void* q, const void* k_cache, const void* v_cache,
  * Mixed batches (section "Scheduler": one step holds decode rows, bound by
  * memory bandwidth, and prefill rows, bound by compute): when the decode
  * rows take even shares and num_tokens - num_seqs >= 1024, the prefill
- * launches run on a second stream that the library makes for the device on
- * the first such call (default priority; kept until the process ends),
- * forked from `stream` after the call's cache write and joined back into
- * `stream` by events before the call returns, while the decode's shares
- * (160 of them, PA_MIXED_DECODE_WGS overrides) run on `stream` and leave
- * CUs to the prefill tiles. Work enqueued on `stream` after the call still
+ * tiles that see many keys run on a second stream that the library makes
+ * for the device on the first such call (default priority; kept until the
+ * process ends), forked from `stream` after the call's cache write and tile
+ * planner and joined back into `stream` by events before the call returns,
+ * while the decode's shares (160 of them, PA_MIXED_DECODE_WGS overrides),
+ * then the tiles that see few keys, run on `stream` and leave CUs to the
+ * long prefill tiles. Work enqueued on `stream` after the call still
  * sees all of its results. Calls made while `stream` is being captured
  * into a graph, calls whose `stream` belongs to a device other than the
  * current one, calls with PA_FORWARD_SERIAL, pa_write_and_forward_noalloc
