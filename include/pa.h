@@ -144,7 +144,11 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * max_query_len_hint <= 16 / (num_q_heads / num_kv_heads) (for instance
  * rows verifying a few speculated tokens) every row takes the decode path
  * (either schedule, chosen as for single-token rows), its q_len * G query
- * columns sharing each K/V block, and no prefill launch is made.
+ * columns sharing each K/V block, and no prefill launch is made. A batch
+ * that makes a prefill launch and has no row longer than 128 keys (by
+ * max_seq_len_hint, else max_blocks_per_seq * 16) runs its single-token rows
+ * on the prefill path too, so no decode launch is made, unless a flag of
+ * pa_forward_ex names the decode schedule.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
  * Tuning overrides, read once per process (for sweeps; out-of-range values
  * are ignored): PA_DECODE_STREAM (0 / 1 = always the partitioned / the
@@ -152,7 +156,9 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * (even-share workgroups, 1..512), PA_DECODE_PART_TOKENS (tokens per decode
  * partition, a multiple of 16, at least 128), PA_DECODE_WAVES (waves per
  * partitioned decode workgroup, 1..16 within the head size's limit),
- * PA_DECODE_PREFETCH (blocks in flight per wave at head_size 64, 2..3).
+ * PA_DECODE_PREFETCH (blocks in flight per wave at head_size 64, 2..3),
+ * PA_SHORT_BATCH_TILES (0 = single-token rows of a batch of short rows keep
+ * the decode launch).
  * Requires block_size == 16, head_size in {64, 128}, num_q_heads /
  * num_kv_heads in {1, 2, 4, 8, 16}. Caller contract: 0 <= q_len <= seq_len
  * <= max_blocks_per_seq * 16 and the first ceil(seq_len / 16) table entries
@@ -230,8 +236,9 @@ int pa_forward_ex(const void* q, const void* k_cache, const void* v_cache,
  * workgroup where the head size needs the registers; the default takes 4),
  * a single launch does both: each row's workgroups write its new token into
  * the caches and read that token from k and v rather than from the slot
- * being written. Otherwise the write is a launch of its own ahead of the
- * forward launches.
+ * being written. A batch with prefill rows writes in the launch of the
+ * tile planner (which the prefill tiles, and any decode launch, follow);
+ * otherwise the write is a launch of its own ahead of the forward launches.
  *
  *   k, v, slot_mapping   as for pa_cache_write (k, v: bf16 [num_tokens,
  *                        num_kv_heads, head_size]; slot_mapping int64

@@ -94,6 +94,7 @@ struct PrefillPlan {
   int32_t* tiles_a;      // [bound_a][2] (sequence, first query row) or -1
   int32_t* tiles_b;      // [bound_b][2]
   int32_t* counts;       // [2] tiles the planner put in lists A and B
+  bool all_rows;         // list single-token rows too (no decode launch follows)
 };
 // The planner (one workgroup), then the tiles it listed; the tiles may go to
 // another stream ordered after the planner.

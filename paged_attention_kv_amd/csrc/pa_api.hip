@@ -204,6 +204,10 @@ bool mixed_overlap_enabled() {
   static const int v = env_int("PA_MIXED_OVERLAP", 0, 1, 1);
   return v == 1;
 }
+bool short_batch_tiles_enabled() {
+  static const int v = env_int("PA_SHORT_BATCH_TILES", 0, 1, 1);
+  return v == 1;
+}
 int32_t mixed_decode_wgs() {
   static const int v = env_int("PA_MIXED_DECODE_WGS", 1, kStreamMaxWgs, kOverlapDecodeWgs);
   return v;
@@ -550,9 +554,17 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   // call returns; not under graph capture, and not for the no-allocation
   // entry point (the side stream is made on first use).
   const bool has_prefill = a.max_query_len > w.qmax;
+  // A batch with prefill rows in which no row is longer than the few-key
+  // tiles' bound (list A stays empty) runs every row, the single-token ones
+  // too, as few-key tiles: the planner and one tile launch, no decode launch.
+  // Not when a flag names the decode schedule; PA_SHORT_BATCH_TILES=0 turns
+  // it off (for comparisons).
+  const bool all_rows = has_prefill && a.max_seq_len <= pa::prefill_split_keys() &&
+                        !(flags & (PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED)) &&
+                        short_batch_tiles_enabled();
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
-  if (has_prefill && dp.stream && !static_scratch && !(flags & PA_FORWARD_SERIAL) &&
+  if (has_prefill && !all_rows && dp.stream && !static_scratch && !(flags & PA_FORWARD_SERIAL) &&
       mixed_overlap_enabled() && (int64_t)num_tokens - num_seqs >= kOverlapMinPrefillTokens &&
       !capturing(st)) {
     side_lock.lock();
@@ -578,6 +590,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     pp.counts = (int32_t*)(ws + w.off_counts);
     // no tile sees more keys than the longest row has: list A stays empty
     if (a.max_seq_len <= pa::prefill_split_keys()) pp.bound_a = 0;
+    pp.all_rows = all_rows;
   }
   if (wr && !fused && has_prefill) {
     hipError_t e = pa::launch_write_and_plan(a, pp, wr->k, wr->v, wr->slot_mapping, wr->k_cache,
@@ -620,6 +633,7 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     hipError_t e = pa::launch_prefill_tiles(a, pp_side, pst);
     if (e != hipSuccess) return join(hip_fail(e, "pa_forward prefill launch"));
   }
+  if (all_rows) return join(PA_OK);
   dp.stream_wgs = side ? std::min(w.stream_wgs, mixed_decode_wgs()) : w.stream_wgs;
   dp.stream_heads = w.stream_heads;
   dp.part_tokens = w.part_tokens;

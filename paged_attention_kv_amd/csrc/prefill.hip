@@ -59,12 +59,15 @@ constexpr int kPlanThreads = 1024;
 // Two tile lists, entry = (sequence, first query row), unused entries -1:
 // list A holds tiles whose rows see more than kSplitKeys keys, each row's
 // heaviest (latest) tiles first; list B the tiles that see at most
-// kSplitKeys keys (they keep P as bf16 hi + lo).
+// kSplitKeys keys (they keep P as bf16 hi + lo). Rows of at least min_ql
+// query tokens are listed: 2 when the decode launch takes the single-token
+// rows, 1 when the tiles take every row.
 // (one workgroup of kPlanThreads threads builds both lists)
 __device__ __forceinline__ void plan_tiles(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
     int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
-    int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts) {
+    int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts,
+    int32_t min_ql) {
   __shared__ int32_t scan_a[kPlanThreads], scan_b[kPlanThreads];
   __shared__ int32_t carry_a, carry_b;
   const int tid = threadIdx.x;
@@ -76,7 +79,7 @@ __device__ __forceinline__ void plan_tiles(
     if (s < S) {
       ql = qsl[s + 1] - qsl[s];
       c = seq_lens[s] - ql;
-      if (ql > 1) {
+      if (ql >= min_ql && ql > 0) {
         const int n = (ql + bq_b - 1) / bq_b;
         // kv_end of B tile t is c + min((t+1)*bq_b, ql): non-decreasing in t
         while (nb < n && c + min((nb + 1) * bq_b, ql) <= kSplitKeys) ++nb;
@@ -135,8 +138,9 @@ __device__ __forceinline__ void plan_tiles(
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
     int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
-    int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts) {
-  plan_tiles(qsl, seq_lens, S, bq_a, bq_b, tiles_a, bound_a, tiles_b, bound_b, counts);
+    int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts,
+    int32_t min_ql) {
+  plan_tiles(qsl, seq_lens, S, bq_a, bq_b, tiles_a, bound_a, tiles_b, bound_b, counts, min_ql);
 }
 
 // The KV write and the planner in one launch (pa_write_and_forward on a
@@ -149,11 +153,11 @@ __global__ __launch_bounds__(kPlanThreads) void write_plan_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ seq_lens, int32_t S,
     int32_t bq_a, int32_t bq_b, int32_t* __restrict__ tiles_a, int32_t bound_a,
     int32_t* __restrict__ tiles_b, int32_t bound_b, int32_t* __restrict__ counts,
-    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    int32_t min_ql, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int64_t* __restrict__ slot_mapping, u32x4* __restrict__ k_cache,
     u32x4* __restrict__ v_cache, int64_t total_chunks, int32_t chunks_per_token) {
   if (blockIdx.x == 0) {  // workgroup-uniform
-    plan_tiles(qsl, seq_lens, S, bq_a, bq_b, tiles_a, bound_a, tiles_b, bound_b, counts);
+    plan_tiles(qsl, seq_lens, S, bq_a, bq_b, tiles_a, bound_a, tiles_b, bound_b, counts, min_ql);
     return;
   }
   const int64_t i = (int64_t)(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
@@ -731,7 +735,7 @@ hipError_t launch_prefill_plan(const ForwardArgs& a, const PrefillPlan& p, hipSt
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
                      a.query_start_loc, a.seq_lens, a.num_seqs, p.tile_queries,
                      p.split_tile_queries, p.tiles_a,
-                     p.bound_a, p.tiles_b, p.bound_b, p.counts);
+                     p.bound_a, p.tiles_b, p.bound_b, p.counts, p.all_rows ? 1 : 2);
   profile_end(PA_KERNEL_PLAN, stream);
   return hipGetLastError();
 }
@@ -750,7 +754,7 @@ hipError_t launch_write_and_plan(const ForwardArgs& a, const PrefillPlan& p, con
   hipLaunchKernelGGL(write_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), 0, stream,
                      a.query_start_loc, a.seq_lens, a.num_seqs, p.tile_queries,
                      p.split_tile_queries, p.tiles_a, p.bound_a, p.tiles_b, p.bound_b, p.counts,
-                     (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
+                     p.all_rows ? 1 : 2, (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
                      (u32x4*)v_cache, total, chunks_per_token);
   profile_end(PA_KERNEL_WRITE_PLAN, stream);
   return hipGetLastError();

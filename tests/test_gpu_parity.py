@@ -722,18 +722,21 @@ def test_write_and_forward_mixed_batch_skips_negative_slots():
     assert_close(one.cpu()[r], want, "mixed rows with slots")
 
 
-@pytest.mark.parametrize("hinted", [True, False])
-def test_short_rows_launch_no_long_tile_list(hinted):
+@pytest.mark.parametrize("hinted,schedule", [(True, None), (False, None), (True, "partitioned"),
+                                             (True, "even")])
+def test_short_rows_launch_no_long_tile_list(hinted, schedule):
     """No row longer than 128 keys (by the hint, or by the table's width when
-    there is none): no tile can see more, so list A is not launched; the
-    rows' tiles all run from list B."""
-    rows = [(40, 20), (1, 50), (7, 0), (100, 27), (1, 3)]
+    there is none): no tile can see more, so list A is not launched. Every
+    row, the single-token ones too, then runs as a few-key tile (the write
+    with the planner, then one tile launch); a flag naming the decode
+    schedule keeps the single-token rows on the decode launch."""
+    rows = [(40, 20), (1, 50), (7, 0), (100, 27), (1, 3), (0, 9), (1, 0), (1, 127)]
     spec = wl.custom("short_rows", 32, 8, 128, rows=rows, seed=93, max_blocks_per_seq=8)
     case = wl.make_case(spec, device=DEV)
-    view = OracleView(case, range(spec.num_seqs))
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
     pa.profile_begin()
     if hinted:
-        out = fused_call(case, max_query_len=100)
+        out = fused_call(case, schedule, max_query_len=100)
     else:
         out = pa.write_and_forward(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache,
                                    case.q, case.block_table, case.seq_lens,
@@ -741,9 +744,31 @@ def test_short_rows_launch_no_long_tile_list(hinted):
         torch.cuda.synchronize()
     per = pa.profile_end()
     assert "prefill" not in per and per["prefill_short"][0] == 1, per
-    assert per["write_plan"][0] == 1 and per["decode"][0] == 1, per
+    assert per["write_plan"][0] == 1, per
+    if schedule is None:
+        assert "decode" not in per and len(per) == 2, per
+    else:
+        assert per["decode"][0] == 1, per
     r, want = view.expect()
     assert_close(out.cpu()[r], want, "short rows")
+
+
+def test_short_batch_of_decode_rows_as_tiles_matches_the_decode_launch():
+    """Many single-token rows of at most 128 keys beside one prompt: the
+    few-key tiles that take them (no decode launch) match the oracle on
+    every row and the decode launch (a schedule flag) to the bar."""
+    rows = [(1, (29 * i) % 128) for i in range(300)] + [(64, 60)]
+    spec = wl.custom("short_decode", 32, 8, 128, rows=rows, seed=95, max_blocks_per_seq=8)
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    tiles = fused_call(case, max_query_len=64).clone()
+    per = pa.profile_end()
+    assert "decode" not in per and per["prefill_short"][0] == 1, per
+    r, want = view.expect()
+    assert_close(tiles.cpu()[r], want, "decode rows as tiles")
+    dec = write_and_forward(case, decode_schedule="partitioned")
+    assert_close(tiles.cpu().float(), dec.cpu().float(), "tiles against the decode launch")
 
 
 def test_nan_poison_outside_context_does_not_leak():
