@@ -182,11 +182,13 @@ def run_steps(pa, inp: StepInputs, steps: int, warmup: int, shared_prefix: bool 
     def step(i):
         st = inp.sets[i % inp.rotations]
         if shared_prefix:
-            # the write, then the shared prefix attended once for all rows
-            pa.cache_write(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache)
-            pa.forward_shared_prefix(st["q"], inp.k_cache, inp.v_cache, st["block_table"],
-                                     inp.seq_lens, inp.qsl, spec.scale, spec.shared_prefix_blocks,
-                                     out=st["out"], max_seq_len=inp.hints["max_seq_len"])
+            # the shared prefix attended once for all rows, the write in its
+            # launch; then the rows' own blocks
+            pa.write_and_forward_shared_prefix(st["k"], st["v"], st["slot_mapping"], inp.k_cache,
+                                               inp.v_cache, st["q"], st["block_table"],
+                                               inp.seq_lens, inp.qsl, spec.scale,
+                                               spec.shared_prefix_blocks, out=st["out"],
+                                               max_seq_len=inp.hints["max_seq_len"])
             return
         pa.write_and_forward(st["k"], st["v"], st["slot_mapping"], inp.k_cache, inp.v_cache,
                              st["q"], st["block_table"], inp.seq_lens, inp.qsl, spec.scale,
@@ -641,7 +643,8 @@ def leg_prefix(pa, args, dev):
             tf = pre_flops / (t["kernels"]["prefix"] * 1e-3) / 1e12
             e["prefix_kernel"] = {"bound": "mfma", "achieved": round(tf, 2),
                                   "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": frac(tf, BF16_PEAK_TFLOPS), "flops": pre_flops}
+                                  "frac": frac(tf, BF16_PEAK_TFLOPS), "flops": pre_flops,
+                                  "note": "its launch also writes the step's new tokens"}
         out[name] = e
     # the workload's step time is that of its faster path, the shared-prefix pass
     out["ms_per_step"] = out["shared_prefix_pass"]["ms_per_step"]

@@ -338,6 +338,38 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
                              void* stream);
 
 /*
+ * The step's KV write and the shared-prefix decode in one call: the same
+ * results as pa_cache_write(k, v, slot_mapping, k_cache, v_cache, num_seqs,
+ * num_kv_heads, head_size, num_blocks, block_size, stream) followed by
+ * pa_forward_shared_prefix(...) (section "Run forward pass": the new tokens
+ * are written through the slot mapping before attention reads them;
+ * section "Prefix Caching" for the shared blocks). The write rides in the
+ * prefix pass's launch, which reads only the prefix's blocks; the rows'
+ * own blocks are read by the launch after it.
+ *
+ *   k, v, slot_mapping   as for pa_cache_write, one token per row (k, v:
+ *                        bf16 [num_seqs, num_kv_heads, head_size];
+ *                        slot_mapping int64 [num_seqs], < 0 skips a token)
+ *   everything else      as for pa_forward_shared_prefix; k_cache, v_cache
+ *                        are written
+ *
+ * Caller contract (not checked), beyond pa_forward_shared_prefix's: no slot
+ * being written lies in the prefix's blocks (each row's new token sits past
+ * the prefix, in a block of its own). Errors as for pa_cache_write and
+ * pa_forward_shared_prefix; on an error nothing is launched.
+ */
+int pa_write_and_forward_shared_prefix(const void* k, const void* v, const int64_t* slot_mapping,
+                                       void* k_cache, void* v_cache, const void* q,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* query_start_loc, float scale, void* out,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_blocks_per_seq,
+                                       int64_t num_blocks, int32_t prefix_blocks,
+                                       int32_t max_seq_len_hint, void* workspace,
+                                       size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
  * Synchronous check of the device-resident metadata that the hot path
  * trusts (for tests and debugging; copies to the host and waits on
  * `stream`). Checks: query_start_loc starts at 0, never decreases and ends at

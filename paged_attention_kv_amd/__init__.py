@@ -17,7 +17,7 @@ from typing import Optional
 import torch
 
 __all__ = ["cache_write", "forward", "write_and_forward", "write_and_forward_noalloc",
-           "forward_shared_prefix",
+           "forward_shared_prefix", "write_and_forward_shared_prefix",
            "forward_workspace_bytes",
            "validate_inputs",
            "kv_block_bytes", "last_error", "version", "library_path", "load_library",
@@ -73,6 +73,10 @@ SIGNATURES = {
     "pa_forward_shared_prefix": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
                                                 _I32, _I32, _I32, _I32, _I32, _I32, _I64, _I32,
                                                 _I32, _P, _SZ, ctypes.c_uint32, _P]),
+    "pa_write_and_forward_shared_prefix": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                          ctypes.c_float, _P, _I32, _I32, _I32,
+                                                          _I32, _I32, _I32, _I64, _I32, _I32, _P,
+                                                          _SZ, ctypes.c_uint32, _P]),
     "pa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32, _I32,
                                   _I32, _I32, _I32, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
     "pa_forward_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _I32, _I32,
@@ -327,17 +331,10 @@ def forward(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
-def forward_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                          block_table: torch.Tensor, seq_lens: torch.Tensor,
-                          query_start_loc: torch.Tensor, scale: float, prefix_blocks: int,
-                          out: Optional[torch.Tensor] = None,
-                          max_seq_len: Optional[int] = None,
-                          workspace: Optional[torch.Tensor] = None,
-                          shared_blocks: bool = False) -> torch.Tensor:
-    """Decode rows (one query token each) whose tables all start with the
-    same ``prefix_blocks`` blocks (pa_forward_shared_prefix): the prefix is
-    attended once for all rows, each row's own blocks after it separately,
-    and the two merged. Returns ``out`` ([S, Hq, D] bf16)."""
+def _shared_prefix_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale,
+                        prefix_blocks, out, max_seq_len, workspace, shared_blocks):
+    """Checks and marshals the arguments of the shared-prefix calls: returns
+    the C call's arguments from ``q`` on, and ``out``."""
     lib = load_library()
     _dev_tensor("q", q, torch.bfloat16, 3)
     for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -362,17 +359,62 @@ def forward_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     need = lib.pa_shared_prefix_workspace_bytes(S, Hq, Hkv, D, MB, prefix_blocks,
                                                 max_seq_len or 0)
     if need == 0:
-        raise ValueError("unsupported sizes for pa_forward_shared_prefix")
+        raise ValueError("unsupported sizes for the shared-prefix call")
     if workspace is None:
         workspace = _workspace(q.get_device(), need)
     elif not workspace.is_cuda or workspace.get_device() != q.get_device():
         raise ValueError("workspace must be on q's device")
-    _check(lib.pa_forward_shared_prefix(
-        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        seq_lens.data_ptr(), query_start_loc.data_ptr(), float(scale), out.data_ptr(), S, Hq,
-        Hkv, D, bs, MB, NB, prefix_blocks, max_seq_len or 0, workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(),
-        FORWARD_SHARED_BLOCKS if shared_blocks else 0, _stream(q)))
+    tail = (q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+            query_start_loc.data_ptr(), float(scale), out.data_ptr(), S, Hq, Hkv, D, bs, MB, NB,
+            prefix_blocks, max_seq_len or 0, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(),
+            FORWARD_SHARED_BLOCKS if shared_blocks else 0, _stream(q))
+    return tail, out
+
+
+def forward_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_table: torch.Tensor, seq_lens: torch.Tensor,
+                          query_start_loc: torch.Tensor, scale: float, prefix_blocks: int,
+                          out: Optional[torch.Tensor] = None,
+                          max_seq_len: Optional[int] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          shared_blocks: bool = False) -> torch.Tensor:
+    """Decode rows (one query token each) whose tables all start with the
+    same ``prefix_blocks`` blocks (pa_forward_shared_prefix): the prefix is
+    attended once for all rows, each row's own blocks after it separately,
+    and the two merged. Returns ``out`` ([S, Hq, D] bf16)."""
+    tail, out = _shared_prefix_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
+                                    scale, prefix_blocks, out, max_seq_len, workspace,
+                                    shared_blocks)
+    _check(load_library().pa_forward_shared_prefix(tail[0], k_cache.data_ptr(),
+                                                   v_cache.data_ptr(), *tail[1:]))
+    return out
+
+
+def write_and_forward_shared_prefix(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                                    k_cache: torch.Tensor, v_cache: torch.Tensor, q: torch.Tensor,
+                                    block_table: torch.Tensor, seq_lens: torch.Tensor,
+                                    query_start_loc: torch.Tensor, scale: float,
+                                    prefix_blocks: int, out: Optional[torch.Tensor] = None,
+                                    max_seq_len: Optional[int] = None,
+                                    workspace: Optional[torch.Tensor] = None,
+                                    shared_blocks: bool = False) -> torch.Tensor:
+    """``cache_write`` then ``forward_shared_prefix`` in one call
+    (pa_write_and_forward_shared_prefix): the write rides in the prefix
+    pass's launch. Returns ``out``."""
+    for n, t in (("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.bfloat16, 3)
+    _dev_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("k, v, slot_mapping and q disagree in token count")
+    if tuple(k.shape[1:]) != tuple(k_cache.shape[2:]):
+        raise ValueError("k must be [T, Hkv, D] matching the caches")
+    tail, out = _shared_prefix_args(q, k_cache, v_cache, block_table, seq_lens, query_start_loc,
+                                    scale, prefix_blocks, out, max_seq_len, workspace,
+                                    shared_blocks)
+    _check(load_library().pa_write_and_forward_shared_prefix(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), *tail))
     return out
 
 

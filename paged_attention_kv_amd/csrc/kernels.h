@@ -126,6 +126,15 @@ struct PrefixPlan {
   int32_t num_parts_max;  // partials per row in the workspace (prefix + suffix)
   float* ws_o;
   float* ws_ml;
+  // The step's KV write in the same launch (write_tokens 0: none): token t
+  // of knew / vnew ([write_tokens][Hkv][D]) goes to slot slot_mapping[t] of
+  // k_cache_w / v_cache_w, never a slot of the prefix's blocks.
+  int32_t write_tokens;
+  const void* knew;
+  const void* vnew;
+  const int64_t* slot_mapping;
+  void* k_cache_w;
+  void* v_cache_w;
 };
 hipError_t launch_prefix(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream);
 

@@ -20,7 +20,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) {
+__attribute__((format(printf, 2, 3))) int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -808,6 +808,118 @@ bool plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, in
   return true;
 }
 
+
+// pa_forward_shared_prefix, with the step's KV write in the prefix launch
+// when wr is given (pa_write_and_forward_shared_prefix; fn names the entry
+// point in errors).
+int shared_prefix_impl(const WriteArgs* wr, const char* fn, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* query_start_loc, float scale, void* out, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                       int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                       int32_t prefix_blocks, int32_t max_seq_len_hint, void* workspace,
+                       size_t workspace_bytes, uint32_t flags, void* stream) {
+  if (flags & ~PA_FORWARD_SHARED_BLOCKS)
+    return fail(PA_ERR_UNSUPPORTED, "%s: unsupported flags 0x%x", fn, flags);
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_SHAPE, "%s: a size is out of range", fn);
+  if (num_q_heads % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn,
+                num_q_heads, num_kv_heads);
+  if (block_size != PA_BLOCK_SIZE)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only %d is built)", fn, block_size,
+                PA_BLOCK_SIZE);
+  if (head_size != 64 && head_size != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_size %d (built: 64, 128)", fn, head_size);
+  if (!supported_group(num_q_heads / num_kv_heads))
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head", fn,
+                num_q_heads / num_kv_heads);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(PA_ERR_SHAPE, "%s: scale is not finite", fn);
+  const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
+  if (prefix_blocks <= 0 || (int64_t)prefix_blocks * PA_BLOCK_SIZE >= max_len)
+    return fail(PA_ERR_SHAPE, "%s: prefix_blocks %d must be >= 1 and leave every row at least "
+                "one key past it (max_seq_len %d)", fn, prefix_blocks, max_len);
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
+    return fail(PA_ERR_NULL, "%s: null pointer argument", fn);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
+    return fail(PA_ERR_ALIGN, "%s: q, caches and out must be 16-byte aligned", fn);
+  PrefixLayout pl;
+  if (!plan_prefix(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq,
+                   prefix_blocks, max_seq_len_hint, &pl))
+    return fail(PA_ERR_SHAPE, "%s: cannot plan the workspace", fn);
+  if (!workspace || workspace_bytes < pl.total)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, pl.total);
+  if (!aligned(workspace, 16))
+    return fail(PA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+
+  pa::ForwardArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = query_start_loc;
+  a.out = out;
+  a.scale = scale;
+  a.num_tokens = num_seqs;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_size = head_size;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = max_len;
+  a.max_query_len = 1;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  pa::PrefixPlan pp = {};
+  pp.chunks = pl.chunks;
+  pp.chunk_keys = pl.chunk_keys;
+  pp.prefix_keys = pl.prefix_keys;
+  pp.num_parts_max = pl.num_parts_max;
+  pp.ws_o = (float*)(ws + pl.off_o);
+  pp.ws_ml = (float*)(ws + pl.off_ml);
+  if (wr) {
+    pp.write_tokens = num_seqs;
+    pp.knew = wr->k;
+    pp.vnew = wr->v;
+    pp.slot_mapping = wr->slot_mapping;
+    pp.k_cache_w = wr->k_cache;
+    pp.v_cache_w = wr->v_cache;
+  }
+  hipError_t e = pa::launch_prefix(a, pp, st);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix prefix launch");
+
+  pa::DecodePlan dp = {};
+  dp.stream = false;
+  dp.part_tokens = pl.part_tokens;
+  dp.num_parts_max = pl.num_parts_max;
+  dp.waves = pl.waves;
+  dp.heads_per_wg = pl.heads_per_wg;
+  dp.prefetch = pl.prefetch;
+  dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
+  dp.ws_o = pp.ws_o;
+  dp.ws_ml = pp.ws_ml;
+  dp.tok_base = pl.prefix_keys;
+  dp.part_base = pl.chunks;
+  dp.qmax = 1;
+  // The last workgroup of each (row, KV head) merges the prefix chunks'
+  // partials with its own row's, through the counters at the start of the
+  // workspace (a row whose own keys fit one partition merges them directly);
+  // rows whose own keys are split into partitions longer than the in-kernel
+  // merge takes (decode_fused_combine) leave every partial to the combine
+  // launch.
+  dp.counters = (int32_t*)ws;
+  dp.fused_combine = decode_fused_combine(num_seqs, num_kv_heads, pl.part_tokens);
+  e = pa::launch_decode(a, dp, st);
+  if (e != hipSuccess) return hip_fail(e, "shared-prefix decode launch");
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -832,101 +944,37 @@ int pa_forward_shared_prefix(const void* q, const void* k_cache, const void* v_c
                              void* workspace, size_t workspace_bytes, uint32_t flags,
                              void* stream) {
   g_last_error.clear();
-  if (flags & ~PA_FORWARD_SHARED_BLOCKS)
-    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: unsupported flags 0x%x", flags);
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
-    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: a size is out of range");
-  if (num_q_heads % num_kv_heads)
-    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: num_q_heads %d is not a multiple of "
-                "num_kv_heads %d", num_q_heads, num_kv_heads);
-  if (block_size != PA_BLOCK_SIZE)
-    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: block_size %d (only %d is "
-                "built)", block_size, PA_BLOCK_SIZE);
-  if (head_size != 64 && head_size != 128)
-    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: head_size %d (built: 64, 128)",
-                head_size);
-  if (!supported_group(num_q_heads / num_kv_heads))
-    return fail(PA_ERR_UNSUPPORTED, "pa_forward_shared_prefix: %d query heads per KV head",
-                num_q_heads / num_kv_heads);
-  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
-    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: scale is not finite");
-  const int32_t max_len = resolved_max_seq_len(max_blocks_per_seq, max_seq_len_hint);
-  if (prefix_blocks <= 0 || (int64_t)prefix_blocks * PA_BLOCK_SIZE >= max_len)
-    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: prefix_blocks %d must be >= 1 and "
-                "leave every row at least one key past it (max_seq_len %d)", prefix_blocks,
-                max_len);
-  if (num_seqs == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !query_start_loc || !out)
-    return fail(PA_ERR_NULL, "pa_forward_shared_prefix: null pointer argument");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(query_start_loc, 4))
-    return fail(PA_ERR_ALIGN, "pa_forward_shared_prefix: q, caches and out must be 16-byte "
-                "aligned");
-  PrefixLayout pl;
-  if (!plan_prefix(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq,
-                   prefix_blocks, max_seq_len_hint, &pl))
-    return fail(PA_ERR_SHAPE, "pa_forward_shared_prefix: cannot plan the workspace");
-  if (!workspace || workspace_bytes < pl.total)
-    return fail(PA_ERR_WORKSPACE, "pa_forward_shared_prefix: workspace of %zu bytes, %zu "
-                "needed", workspace ? workspace_bytes : (size_t)0, pl.total);
-  if (!aligned(workspace, 16))
-    return fail(PA_ERR_ALIGN, "pa_forward_shared_prefix: workspace must be 16-byte aligned");
+  return shared_prefix_impl(nullptr, "pa_forward_shared_prefix", q, k_cache, v_cache,
+                            block_table, seq_lens, query_start_loc, scale, out, num_seqs,
+                            num_q_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                            num_blocks, prefix_blocks, max_seq_len_hint, workspace,
+                            workspace_bytes, flags, stream);
+}
 
-  pa::ForwardArgs a;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.query_start_loc = query_start_loc;
-  a.out = out;
-  a.scale = scale;
-  a.num_tokens = num_seqs;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_size = head_size;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_seq_len = max_len;
-  a.max_query_len = 1;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-
-  pa::PrefixPlan pp;
-  pp.chunks = pl.chunks;
-  pp.chunk_keys = pl.chunk_keys;
-  pp.prefix_keys = pl.prefix_keys;
-  pp.num_parts_max = pl.num_parts_max;
-  pp.ws_o = (float*)(ws + pl.off_o);
-  pp.ws_ml = (float*)(ws + pl.off_ml);
-  hipError_t e = pa::launch_prefix(a, pp, st);
-  if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix prefix launch");
-
-  pa::DecodePlan dp = {};
-  dp.stream = false;
-  dp.part_tokens = pl.part_tokens;
-  dp.num_parts_max = pl.num_parts_max;
-  dp.waves = pl.waves;
-  dp.heads_per_wg = pl.heads_per_wg;
-  dp.prefetch = pl.prefetch;
-  dp.stream_v = !(flags & PA_FORWARD_SHARED_BLOCKS);
-  dp.ws_o = pp.ws_o;
-  dp.ws_ml = pp.ws_ml;
-  dp.tok_base = pl.prefix_keys;
-  dp.part_base = pl.chunks;
-  dp.qmax = 1;
-  // The last workgroup of each (row, KV head) merges the prefix chunks'
-  // partials with its own row's, through the counters at the start of the
-  // workspace (a row whose own keys fit one partition merges them directly);
-  // rows whose own keys are split into partitions longer than the in-kernel
-  // merge takes (decode_fused_combine) leave every partial to the combine
-  // launch.
-  dp.counters = (int32_t*)ws;
-  dp.fused_combine = decode_fused_combine(num_seqs, num_kv_heads, pl.part_tokens);
-  e = pa::launch_decode(a, dp, st);
-  if (e != hipSuccess) return hip_fail(e, "pa_forward_shared_prefix decode launch");
-  return PA_OK;
+int pa_write_and_forward_shared_prefix(const void* k, const void* v, const int64_t* slot_mapping,
+                                       void* k_cache, void* v_cache, const void* q,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const int32_t* query_start_loc, float scale, void* out,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_blocks_per_seq,
+                                       int64_t num_blocks, int32_t prefix_blocks,
+                                       int32_t max_seq_len_hint, void* workspace,
+                                       size_t workspace_bytes, uint32_t flags, void* stream) {
+  g_last_error.clear();
+  if (num_seqs > 0) {
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+      return fail(PA_ERR_NULL, "pa_write_and_forward_shared_prefix: null k/v/slot_mapping/cache");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+      return fail(PA_ERR_ALIGN, "pa_write_and_forward_shared_prefix: k and v must be 16-byte "
+                  "aligned");
+  }
+  const WriteArgs wr{k, v, slot_mapping, k_cache, v_cache};
+  return shared_prefix_impl(&wr, "pa_write_and_forward_shared_prefix", q, k_cache, v_cache,
+                            block_table, seq_lens, query_start_loc, scale, out, num_seqs,
+                            num_q_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                            num_blocks, prefix_blocks, max_seq_len_hint, workspace,
+                            workspace_bytes, flags, stream);
 }
 
 int pa_probe_block_read(const void* k_cache, const void* v_cache, const int32_t* block_table,

@@ -216,6 +216,18 @@ struct PrefixArgs {
   int32_t row_tiles;      // ceil(num_seqs / tile rows)
   int32_t chunks;
   int32_t num_tokens;     // q rows (a row's token index is clamped below it)
+  // The last tile_grid workgroups take the tiles; those before them write
+  // the step's new tokens (write_chunks 16-byte chunks of K and of V, as
+  // the cache-write kernel does). The tiles read only the prefix's blocks,
+  // which hold no slot being written.
+  int32_t tile_grid;
+  int32_t chunks_per_token;
+  int64_t write_chunks;
+  const u32x4* knew;
+  const u32x4* vnew;
+  const int64_t* slot_mapping;
+  u32x4* k_cache_w;
+  u32x4* v_cache_w;
 };
 
 template <int D, int G, int MODE>
@@ -597,9 +609,23 @@ __global__ __launch_bounds__((MODE == kListB ? kWavesB : MODE == kPrefix ? kWave
 
   const int nwg = gridDim.x;
   if (PREFIX) {
+    // The writers come first in the grid: they are dispatched first and
+    // hold their CUs for one load round trip, so a few tiles start that much
+    // later (with the writers after the tiles, they wait for CUs that tiles
+    // free and lengthen the launch's tail: 60.2 against 58.4 us per step on
+    // the prefix-shared workload, the two-call sequence 61.4).
+    const int nwrite = (int)gridDim.x - pfx.tile_grid;
+    const int bid = (int)blockIdx.x - nwrite;
+    if (bid < 0) {  // workgroup-uniform: the KV write
+      const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+      if (i < pfx.write_chunks)
+        write_kv_chunk(pfx.knew, pfx.vnew, pfx.slot_mapping, pfx.k_cache_w, pfx.v_cache_w, i,
+                       pfx.chunks_per_token);
+      return;
+    }
     // XCD-aware order: the row tiles of one (KV head, chunk) are
     // consecutive logical tasks, so they share the chunk's K/V in one L2.
-    const int logical = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+    const int logical = (bid % 8) * (pfx.tile_grid / 8) + bid / 8;
     const int rt = logical % pfx.row_tiles;
     const int rest = logical / pfx.row_tiles;
     const int chunk = rest % pfx.chunks;
@@ -677,11 +703,16 @@ template <int D, int G>
 hipError_t launch_prefix_g(const ForwardArgs& a, const PrefixPlan& p, hipStream_t stream) {
   constexpr int BQ = 16 * kRowTiles * kWavesP / G;
   const float scale_log2 = a.scale * 1.4426950408889634f;
-  PrefixArgs x{p.ws_o, p.ws_ml, p.num_parts_max, p.chunk_keys, p.prefix_keys, a.num_seqs,
-               (a.num_seqs + BQ - 1) / BQ, p.chunks, a.num_tokens};
-  const int64_t tasks = (int64_t)x.row_tiles * p.chunks * a.num_kv_heads;
-  const int64_t grid = (tasks + 7) / 8 * 8;
+  const int64_t tasks = (int64_t)((a.num_seqs + BQ - 1) / BQ) * p.chunks * a.num_kv_heads;
+  const int64_t tile_grid = (tasks + 7) / 8 * 8;
+  const int32_t chunks_per_token = a.num_kv_heads * a.head_size / 8;
+  const int64_t write_chunks = p.write_tokens > 0 ? (int64_t)p.write_tokens * chunks_per_token : 0;
+  const int64_t grid = tile_grid + (write_chunks + kWavesP * kWave - 1) / (kWavesP * kWave);
   if (grid > INT32_MAX) return hipErrorInvalidValue;
+  PrefixArgs x{p.ws_o, p.ws_ml, p.num_parts_max, p.chunk_keys, p.prefix_keys, a.num_seqs,
+               (a.num_seqs + BQ - 1) / BQ, p.chunks, a.num_tokens, (int32_t)tile_grid,
+               chunks_per_token, write_chunks, (const u32x4*)p.knew, (const u32x4*)p.vnew,
+               p.slot_mapping, (u32x4*)p.k_cache_w, (u32x4*)p.v_cache_w};
   profile_begin(PA_KERNEL_PREFIX, stream);
   hipLaunchKernelGGL((prefill_tile_kernel<D, G, kPrefix>), dim3((unsigned)grid),
                      dim3(kWavesP * kWave), 0, stream, (const uint16_t*)a.q,

@@ -174,6 +174,39 @@ def test_shared_prefix_workspace(lib):
                                                 s.max_blocks_per_seq, 0) == 0
 
 
+def test_shared_prefix_calls_reject_bad_arguments(lib):
+    """Both shared-prefix entry points check their host arguments alike (the
+    write-and-forward one also its k / v / slot_mapping) and launch nothing
+    on an error or an empty batch."""
+    def sp(write, **kw):
+        a = dict(k=FAKE, v=FAKE, slot=FAKE, q=FAKE, S=8, Hq=32, Hkv=8, D=128, bs=16, MB=20,
+                 NB=1000, pb=4, msl=0, ws=FAKE, wsb=1 << 30, flags=0)
+        a.update(kw)
+        tail = (a["q"], FAKE, FAKE, FAKE, 0.125, FAKE, a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                a["MB"], a["NB"], a["pb"], a["msl"], a["ws"], a["wsb"], a["flags"], None)
+        if write:
+            return lib.pa_write_and_forward_shared_prefix(a["k"], a["v"], a["slot"], FAKE, FAKE,
+                                                          *tail)
+        return lib.pa_forward_shared_prefix(tail[0], FAKE, FAKE, *tail[1:])
+    for write in (False, True):
+        name = "pa_write_and_forward_shared_prefix" if write else "pa_forward_shared_prefix"
+        assert sp(write, q=NULL) == -1
+        assert sp(write, Hq=30) == -2
+        assert sp(write, D=96) == -3
+        assert sp(write, bs=8) == -3
+        assert sp(write, pb=0) == -2
+        assert sp(write, pb=20) == -2         # no key left past the prefix
+        assert sp(write, flags=2) == -3       # only PA_FORWARD_SHARED_BLOCKS
+        assert sp(write, ws=NULL) == -5
+        assert sp(write, wsb=16) == -5
+        assert pa.last_error().startswith(name), pa.last_error()
+        assert sp(write, S=0) == 0            # empty batch: no launch
+    assert sp(True, k=NULL) == -1
+    assert sp(True, slot=NULL) == -1
+    assert sp(True, v=FAKE + 8) == -4
+    assert sp(True, k=NULL, S=0) == 0         # nothing to write
+
+
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define PA_BLOCK_SIZE (\d+)", text).group(1)) == pa.BLOCK_SIZE

@@ -329,17 +329,24 @@ def shared_prefix_call(case, prefix_blocks, **kw):
 
 def test_shared_prefix_workload_all_rows():
     """The prefix-shared decode workload (256 rows, 256 shared blocks + 8 own
-    blocks each): every row against the oracle, and close to the per-row
+    blocks each) as the benchmark times it, one
+    pa_write_and_forward_shared_prefix call: two launches, the written
+    blocks bit-exact against ref_cache_write and every other block of the
+    pool unchanged; every row against the oracle, and close to the per-row
     decode path."""
     spec = wl.config(5)
     banner("shared-prefix pass on workload 5 (256 rows, 256-block shared prefix)")
     case = wl.make_case(spec, device=DEV)
     view = OracleView(case, range(spec.num_seqs))
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
     pa.profile_begin()
-    out = shared_prefix_call(case, spec.shared_prefix_blocks).clone()
+    out = fused_shared_prefix_call(case, spec.shared_prefix_blocks).clone()
     per = pa.profile_end()
-    # the decode launch merges the prefix chunks' partials itself
-    assert per["prefix"][0] == 1 and per["decode"][0] == 1 and "combine" not in per, per
+    # the prefix launch writes the new tokens; the decode launch merges the
+    # prefix chunks' partials itself
+    assert set(per) == {"prefix", "decode"}, per
+    assert per["prefix"][0] == 1 and per["decode"][0] == 1, per
+    assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
     rows, want = view.expect()
     assert_close(out.cpu()[rows], want, "shared prefix")
     ref = write_and_forward(case, shared_blocks=True)
@@ -366,25 +373,73 @@ SHARED_PREFIX_CASES = [
 ]
 
 
+def fused_shared_prefix_call(case, prefix_blocks, **kw):
+    out = pa.write_and_forward_shared_prefix(case.k, case.v, case.slot_mapping, case.k_cache,
+                                             case.v_cache, case.q, case.block_table,
+                                             case.seq_lens, case.query_start_loc, case.scale,
+                                             prefix_blocks, max_seq_len=max(case.spec.seq_lens),
+                                             **kw)
+    torch.cuda.synchronize()
+    return out
+
+
 @pytest.mark.parametrize("name,hq,hkv,d,pb,own", SHARED_PREFIX_CASES,
                          ids=[c[0] for c in SHARED_PREFIX_CASES])
 def test_shared_prefix_cases(name, hq, hkv, d, pb, own):
     """Prefix lengths that end inside a 64-key tile and a chunk, rows past
     one tile of sequences, one-block prefixes, every group size: all rows
-    against the oracle; two calls give identical bits."""
+    against the oracle; two calls give identical bits. The same step
+    through pa_write_and_forward_shared_prefix (the write in the prefix
+    launch) leaves the pool as ref_cache_write does, every other block
+    unchanged, and the same output bits."""
     rows = [(1, 16 * pb + n - 1) for n in own]
     spec = wl.custom(name, hq, hkv, d, rows=rows, seed=120 + pb, shared_prefix_blocks=pb)
     banner(f"shared prefix {name}: S={spec.num_seqs} prefix={pb} blocks Hq={hq} Hkv={hkv} D={d}")
     case = wl.make_case(spec, device=DEV)
     view = OracleView(case, range(spec.num_seqs))
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    pa.profile_begin()
+    fused = fused_shared_prefix_call(case, pb).clone()
+    per = pa.profile_end()
+    assert "cache_write" not in per and per["prefix"][0] == 1 and per["decode"][0] == 1, per
+    assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
+    case.k_cache.copy_(k0)
+    case.v_cache.copy_(v0)
     out = shared_prefix_call(case, pb).clone()
     out2 = pa.forward_shared_prefix(case.q, case.k_cache, case.v_cache, case.block_table,
                                     case.seq_lens, case.query_start_loc, case.scale, pb,
                                     max_seq_len=max(spec.seq_lens))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    assert torch.equal(fused.view(torch.int16), out.view(torch.int16)), "fused write differs"
     r, want = view.expect()
     assert_close(out.cpu()[r], want, name)
+
+
+def test_write_and_forward_shared_prefix_skips_negative_slots():
+    """Rows whose new token has slot < 0: the fused call writes nothing for
+    them and reads their last key from the cache, as the two-call sequence
+    does (pool and output bit-identical); the other rows match the oracle."""
+    pb = 5
+    rows = [(1, 16 * pb + n - 1) for n in (3, 17, 40, 1, 129, 64)]
+    spec = wl.custom("sp_negslot", 32, 8, 128, rows=rows, seed=131, shared_prefix_blocks=pb)
+    case = wl.make_case(spec, device=DEV)
+    slots = case.slot_mapping.clone()
+    slots[1] = -1
+    slots[4] = -7
+    case.slot_mapping = slots
+    view = OracleView(case, [0, 2, 3, 5])
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    one = fused_shared_prefix_call(case, pb).clone()
+    kc, vc = case.k_cache.clone(), case.v_cache.clone()
+    case.k_cache.copy_(k0)
+    case.v_cache.copy_(v0)
+    two = shared_prefix_call(case, pb).clone()
+    assert torch.equal(kc.view(torch.int16), case.k_cache.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), case.v_cache.view(torch.int16))
+    assert torch.equal(one.view(torch.int16), two.view(torch.int16))
+    r, want = view.expect()
+    assert_close(one.cpu()[r], want, "shared prefix rows with slots")
 
 
 def test_shared_prefix_rejects_bad_arguments():
