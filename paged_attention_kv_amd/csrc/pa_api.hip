@@ -85,8 +85,10 @@ int env_int(const char* name, int lo, int hi, int dflt) {
   return (v >= lo && v <= hi) ? v : dflt;
 }
 
+// (max_blocks_per_seq <= kMaxBlocksPerSeq, checked by the planners)
+constexpr int32_t kMaxBlocksPerSeq = INT32_MAX / PA_BLOCK_SIZE;
 int32_t resolved_max_seq_len(int32_t max_blocks_per_seq, int32_t hint) {
-  const int32_t cap = max_blocks_per_seq * PA_BLOCK_SIZE;
+  const int32_t cap = std::min(max_blocks_per_seq, kMaxBlocksPerSeq) * PA_BLOCK_SIZE;
   return hint > 0 ? std::min(hint, cap) : cap;
 }
 
@@ -221,7 +223,8 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_size, int32_t max_blocks_per_seq,
                     int32_t max_query_len_hint, int32_t max_seq_len_hint, WorkspaceLayout* out) {
   if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      head_size <= 0 || max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads)
+      head_size <= 0 || max_blocks_per_seq <= 0 || max_blocks_per_seq > kMaxBlocksPerSeq ||
+      num_q_heads % num_kv_heads)
     return false;
   const int32_t group = num_q_heads / num_kv_heads;
   if (!supported_group(group)) return false;
@@ -250,9 +253,12 @@ bool plan_workspace(int32_t num_tokens, int32_t num_seqs, int32_t num_q_heads,
   w.tile_queries = prefill_tile_queries(group);
   const int32_t bq_b = prefill_split_tile_queries(group);
   // Each row adds at most one partial tile per list: sum ceil(ql/BQ) <= T/BQ + S.
-  w.bound_a = (int32_t)((int64_t)(num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs);
-  w.bound_b = (int32_t)std::min<int64_t>((int64_t)(num_tokens + bq_b - 1) / bq_b + num_seqs,
-                                         (int64_t)num_seqs * prefill_split_tiles_per_row(group));
+  const int64_t bound_a = ((int64_t)num_tokens + w.tile_queries - 1) / w.tile_queries + num_seqs;
+  const int64_t bound_b = std::min<int64_t>(((int64_t)num_tokens + bq_b - 1) / bq_b + num_seqs,
+                                            (int64_t)num_seqs * prefill_split_tiles_per_row(group));
+  if (bound_a > INT32_MAX || bound_b > INT32_MAX) return false;
+  w.bound_a = (int32_t)bound_a;
+  w.bound_b = (int32_t)bound_b;
   w.off_ctr = 0;
   w.off_o = round_up((size_t)kCounterSlots * sizeof(int32_t), kAlign);
   w.off_ml = round_up(w.off_o + dec_o * sizeof(float), kAlign);
@@ -580,9 +586,10 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
     pp.tile_queries = w.tile_queries;
     pp.split_tile_queries = pa::prefill_split_tile_queries(num_q_heads / num_kv_heads);
     const int64_t by_hint_a =
-        (int64_t)num_seqs * ((a.max_query_len + w.tile_queries - 1) / w.tile_queries);
+        (int64_t)num_seqs * (((int64_t)a.max_query_len + w.tile_queries - 1) / w.tile_queries);
     const int64_t by_hint_b =
-        (int64_t)num_seqs * ((a.max_query_len + pp.split_tile_queries - 1) / pp.split_tile_queries);
+        (int64_t)num_seqs *
+        (((int64_t)a.max_query_len + pp.split_tile_queries - 1) / pp.split_tile_queries);
     pp.bound_a = (int32_t)std::min<int64_t>(w.bound_a, by_hint_a);
     pp.bound_b = (int32_t)std::min<int64_t>(w.bound_b, by_hint_b);
     pp.tiles_a = (int32_t*)(ws + w.off_tiles_a);
@@ -759,8 +766,8 @@ bool plan_prefix(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, in
                  int32_t max_blocks_per_seq, int32_t prefix_blocks, int32_t max_seq_len_hint,
                  PrefixLayout* out) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_q_heads % num_kv_heads || prefix_blocks <= 0 ||
-      prefix_blocks >= max_blocks_per_seq)
+      max_blocks_per_seq <= 0 || max_blocks_per_seq > kMaxBlocksPerSeq ||
+      num_q_heads % num_kv_heads || prefix_blocks <= 0 || prefix_blocks >= max_blocks_per_seq)
     return false;
   const int32_t group = num_q_heads / num_kv_heads;
   if (!supported_group(group)) return false;

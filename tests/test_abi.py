@@ -174,6 +174,16 @@ def test_shared_prefix_workspace(lib):
                                                 s.max_blocks_per_seq, 0) == 0
 
 
+def test_table_width_past_the_int32_token_range_is_rejected(lib):
+    """max_blocks_per_seq * 16 must stay within int32 tokens: wider tables
+    plan no workspace and the calls fail before launching."""
+    for mb in (1 << 27, (1 << 31) - 1):
+        assert lib.pa_forward_workspace_bytes(8, 2, 32, 4, 64, mb, 0, 100) == 0
+        assert lib.pa_shared_prefix_workspace_bytes(2, 32, 4, 64, mb, 1, 100) == 0
+        assert fw(lib, MB=mb) == -2
+    assert lib.pa_forward_workspace_bytes(8, 2, 32, 4, 64, (1 << 27) - 1, 0, 100) > 0
+
+
 def test_shared_prefix_calls_reject_bad_arguments(lib):
     """Both shared-prefix entry points check their host arguments alike (the
     write-and-forward one also its k / v / slot_mapping) and launch nothing
