@@ -41,6 +41,7 @@ import math
 import os
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -648,6 +649,27 @@ def leg_prefix(pa, args, dev):
         out[name] = e
     # the workload's step time is that of its faster path, the shared-prefix pass
     out["ms_per_step"] = out["shared_prefix_pass"]["ms_per_step"]
+    # the rows' own blocks (past the prefix) read whole with no arithmetic:
+    # the memory system's rate for the rows' pass of the shared-prefix call
+    P = spec.shared_prefix_blocks
+    own_spec = wl.Spec("own_blocks", spec.num_q_heads, spec.num_kv_heads, spec.head_size,
+                       num_blocks=spec.num_blocks, max_blocks_per_seq=spec.max_blocks_per_seq - P,
+                       q_lens=spec.q_lens,
+                       seq_lens=tuple(L - P * spec.block_size for L in spec.seq_lens),
+                       seed_layout=spec.seed_layout, seed_values=spec.seed_values)
+    own = types.SimpleNamespace(
+        spec=own_spec, k_cache=inp.k_cache, v_cache=inp.v_cache, rotations=inp.rotations,
+        seq_lens=torch.tensor(own_spec.seq_lens, dtype=torch.int32, device=dev),
+        sets=[{"block_table": st["block_table"][:, P:].contiguous()} for st in inp.sets])
+    pms, pshape, pbytes = run_read_probe(pa, own, args.steps, args.warmup)
+    rows_us = out["shared_prefix_pass"]["kernel_avg_us"].get("decode")
+    out["own_blocks_read_probe"] = {
+        "what": "the rows' own blocks past the prefix read whole with no arithmetic "
+                "(pa_probe_block_read), best of %d launch shapes" % len(PROBE_SHAPES),
+        "us": round(pms * 1e3, 3), "bytes": pbytes,
+        "gbs": round(pbytes / (pms * 1e-3) / 1e9, 1),
+        "rows_pass_us": rows_us,
+        "note": "the rows' pass also reads the prefix chunks' partials and merges them"}
     return out
 
 

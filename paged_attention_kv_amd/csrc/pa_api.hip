@@ -451,7 +451,8 @@ bool capturing(hipStream_t st) {
   return cs != hipStreamCaptureStatusNone;
 }
 
-// The step's KV write when it travels with the forward (pa_write_and_forward).
+// The step's KV write when it travels with the forward (pa_write_and_forward,
+// pa_write_and_forward_shared_prefix).
 struct WriteArgs {
   const void* k;
   const void* v;
@@ -463,7 +464,8 @@ struct WriteArgs {
 // pa_forward_ex, optionally preceded by the step's KV write (wr): fused into
 // the decode launch when every row is a decode row (max_query_len_hint == 1),
 // the rows take the partitioned schedule and its waves fit the fused
-// kernel's bound, else a cache-write launch first.
+// kernel's bound; into the tile planner's launch when the batch has prefill
+// rows; else a cache-write launch first.
 int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_table, const int32_t* seq_lens,
                  const int32_t* query_start_loc, float scale, void* out, int32_t num_tokens,
