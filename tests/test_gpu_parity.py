@@ -488,6 +488,32 @@ def test_sweep_full_oracle(d, hq, hkv):
     assert_close(out.cpu()[r], want, spec.name)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", SWEEP_HEADS)
+def test_sweep_short_batch_all_rows_as_tiles(d, hq, hkv):
+    """Batches whose rows are all at most 128 keys long, mixing single-token
+    rows with chunks: every row runs as a few-key tile (no decode launch),
+    each group size and head size against the oracle."""
+    r = random.Random(hash(("short", d, hq, hkv)) % 1000)
+    rows = []
+    for _ in range(12):
+        ql = r.choice([0, 1, 1, 1, 2, 5, 16, 17, 33, 100])
+        c = r.randint(0, 128 - max(ql, 1))
+        rows.append((ql, c if ql or c else 1))
+    rows.append((40, 3))  # at least one chunk, so a tile launch is made
+    spec = wl.custom(f"short_d{d}_{hq}x{hkv}", hq, hkv, d, rows=rows, seed=300 + hq + d,
+                     max_blocks_per_seq=8)
+    banner(f"short batch D={d} Hq={hq} Hkv={hkv} rows={rows}")
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, [s for s in range(spec.num_seqs) if spec.q_lens[s] > 0])
+    pa.profile_begin()
+    out = write_and_forward(case)
+    per = pa.profile_end()
+    assert "decode" not in per and "prefill" not in per and per["prefill_short"][0] == 1, per
+    rr, want = view.expect()
+    assert_close(out.cpu()[rr], want, spec.name)
+
+
 # The longest rows here: 131072 keys (8192 table entries) in one row, as a
 # decode row on every schedule (beside a short one), and as a 64-token chunk
 # at the end of that context (first, middle and last query rows checked).
