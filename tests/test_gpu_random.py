@@ -81,3 +81,39 @@ def test_random_batch_against_the_oracle(seed):
     assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
     r, want = view.expect()
     assert_close(out.cpu()[r], want, spec.name)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shared_prefix_batch_against_the_oracle(seed):
+    """Seeded random shared-prefix batches (head counts, head size, prefix
+    length, row count, each row's own tokens past the prefix), through
+    pa_write_and_forward_shared_prefix or pa_cache_write then
+    pa_forward_shared_prefix: every row against the oracle, the pool bit
+    for bit."""
+    r = random.Random(9000 + seed)
+    hq, hkv = r.choice(HEADS)
+    d = r.choice([64, 128])
+    pb = r.choice([1, 2, 7, 16, 33, 64])
+    own = [r.choice([1, 2, 15, 16, 17, r.randint(1, 600)]) for _ in range(r.randint(1, 300))]
+    rows = [(1, 16 * pb + n - 1) for n in own]
+    spec = wl.custom(f"random_sp{seed}", hq, hkv, d, rows=rows, seed=9100 + seed,
+                     shared_prefix_blocks=pb)
+    fused = r.random() < 0.5
+    print(f"\n[case] random shared prefix {seed}: Hq={hq} Hkv={hkv} D={d} prefix={pb} "
+          f"rows={len(rows)} fused={fused}", flush=True)
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    k0, v0 = case.k_cache.clone(), case.v_cache.clone()
+    args = (case.q, case.block_table, case.seq_lens, case.query_start_loc, case.scale, pb)
+    if fused:
+        out = pa.write_and_forward_shared_prefix(case.k, case.v, case.slot_mapping, case.k_cache,
+                                                 case.v_cache, *args,
+                                                 max_seq_len=max(spec.seq_lens))
+    else:
+        pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
+        out = pa.forward_shared_prefix(case.q, case.k_cache, case.v_cache, *args[1:],
+                                       max_seq_len=max(spec.seq_lens))
+    torch.cuda.synchronize()
+    assert_pool_written(case.k_cache, case.v_cache, k0, v0, case.k, case.v, case.slot_mapping)
+    rr, want = view.expect()
+    assert_close(out.cpu()[rr], want, spec.name)
