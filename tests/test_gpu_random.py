@@ -2,9 +2,10 @@
 draws head counts, head size, a mix of rows (empty, decode, a few query
 tokens, chunks with and without prior context), the length hints (tight,
 none, loose), the decode schedule flag, the serial flag and the entry point
-(pa_write_and_forward, or pa_cache_write then pa_forward_ex). Every row with
-query tokens is checked against the oracle to the same bar as the other
-parity tests, and the pool's written blocks bit for bit."""
+(pa_write_and_forward, or pa_cache_write then pa_forward_ex); and random
+shared-prefix batches through both shared-prefix entry points. Every row
+with query tokens is checked against the oracle to the same bar as the
+other parity tests, and the pool's written blocks bit for bit."""
 
 import random
 
