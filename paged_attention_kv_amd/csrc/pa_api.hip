@@ -568,7 +568,8 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   // Not when a flag names the decode schedule; PA_SHORT_BATCH_TILES=0 turns
   // it off (for comparisons).
   const bool all_rows = has_prefill && a.max_seq_len <= pa::prefill_split_keys() &&
-                        !(flags & (PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED)) &&
+                        !(flags &
+                          (PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED)) &&
                         short_batch_tiles_enabled();
   std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
   SideStream* side = nullptr;
@@ -861,7 +862,8 @@ int shared_prefix_impl(const WriteArgs* wr, const char* fn, const void* q, const
                    prefix_blocks, max_seq_len_hint, &pl))
     return fail(PA_ERR_SHAPE, "%s: cannot plan the workspace", fn);
   if (!workspace || workspace_bytes < pl.total)
-    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, pl.total);
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, pl.total);
   if (!aligned(workspace, 16))
     return fail(PA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
 

@@ -785,8 +785,8 @@ hipError_t launch_write_and_plan(const ForwardArgs& a, const PrefillPlan& p, con
   hipLaunchKernelGGL(write_plan_kernel, dim3((unsigned)blocks), dim3(kPlanThreads), 0, stream,
                      a.query_start_loc, a.seq_lens, a.num_seqs, p.tile_queries,
                      p.split_tile_queries, p.tiles_a, p.bound_a, p.tiles_b, p.bound_b, p.counts,
-                     p.all_rows ? 1 : 2, (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
-                     (u32x4*)v_cache, total, chunks_per_token);
+                     p.all_rows ? 1 : 2, (const u32x4*)k, (const u32x4*)v, slot_mapping,
+                     (u32x4*)k_cache, (u32x4*)v_cache, total, chunks_per_token);
   profile_end(PA_KERNEL_WRITE_PLAN, stream);
   return hipGetLastError();
 }
