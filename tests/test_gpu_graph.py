@@ -7,8 +7,9 @@ replay's own q, k and v written into it by the oracle). Covers the fused
 decode launch, partitioned rows merged in the kernel (arrival counters, reset by the kernels
 themselves, so replays start from zero) or by the combine launch, the even-share schedule, a mixed
 step with prefill tiles and their device planner, rows of four query tokens
-on both decode schedules, the shared-prefix pass, and several steps
-in one graph."""
+on both decode schedules, a batch of short rows run as few-key tiles, the
+shared-prefix pass (with the step's write in its launch, and without), and
+several steps in one graph."""
 
 import pytest
 import torch
@@ -33,6 +34,9 @@ CASES = [
     # rows of four query tokens (speculative verify) on each decode schedule
     ("verify_even", 32, 8, 128, [(4, 1500 + 97 * i) for i in range(80)], "even"),
     ("verify_partitioned", 32, 8, 64, [(4, 300 + 53 * i) for i in range(40)], "partitioned"),
+    # no row past 128 keys: the write with the planner, then every row as a
+    # few-key tile (no decode launch)
+    ("short_tiles", 32, 8, 128, [(1, 50), (20, 30), (1, 100), (7, 8), (1, 127), (40, 60)], None),
 ]
 
 
@@ -128,23 +132,33 @@ def test_graph_of_several_steps_matches_eager():
         _ = (case.q.float() @ case.q.float()[:1].transpose(1, 2).contiguous()).sum()
 
 
-def test_graph_replays_of_the_shared_prefix_pass_match_eager():
+@pytest.mark.parametrize("fused", [False, True], ids=["forward", "write_and_forward"])
+def test_graph_replays_of_the_shared_prefix_pass_match_eager(fused):
     """The shared-prefix pass (prefix tiles, then the rows' own blocks with
-    the merge in the kernel) captured and replayed with new queries."""
+    the merge in the kernel) captured and replayed with new queries; with
+    the step's write in the prefix launch, new keys and values too."""
     pb = 24
     rows = [(1, 16 * pb + own - 1) for own in (1, 17, 40, 200, 5, 64)]
     spec = wl.custom("prefix_graph", 32, 8, 128, rows=rows, seed=181, shared_prefix_blocks=pb)
-    print(f"\n[case] graph replay shared-prefix pass: S={spec.num_seqs}", flush=True)
+    print(f"\n[case] graph replay shared-prefix pass: S={spec.num_seqs} fused={fused}", flush=True)
     case = wl.make_case(spec, device=DEV)
     view = OracleView(case, range(spec.num_seqs))
-    pa.cache_write(case.k, case.v, case.slot_mapping, case.k_cache, case.v_cache)
-    q = case.q.clone()
+    q, k, v = case.q.clone(), case.k.clone(), case.v.clone()
+    if not fused:
+        pa.cache_write(k, v, case.slot_mapping, case.k_cache, case.v_cache)
     out = torch.empty_like(q)
     ms = max(spec.seq_lens)
 
     def step(o):
-        pa.forward_shared_prefix(q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                 case.query_start_loc, case.scale, pb, out=o, max_seq_len=ms)
+        if fused:
+            pa.write_and_forward_shared_prefix(k, v, case.slot_mapping, case.k_cache,
+                                               case.v_cache, q, case.block_table, case.seq_lens,
+                                               case.query_start_loc, case.scale, pb, out=o,
+                                               max_seq_len=ms)
+        else:
+            pa.forward_shared_prefix(q, case.k_cache, case.v_cache, case.block_table,
+                                     case.seq_lens, case.query_start_loc, case.scale, pb, out=o,
+                                     max_seq_len=ms)
 
     step(out)
     torch.cuda.synchronize()
@@ -155,6 +169,9 @@ def test_graph_replays_of_the_shared_prefix_pass_match_eager():
     ref = torch.empty_like(out)
     for i in range(4):
         q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(q.dtype))
+        if fused:
+            k.copy_(torch.randn(k.shape, generator=gen, device=DEV).to(k.dtype))
+            v.copy_(torch.randn(v.shape, generator=gen, device=DEV).to(v.dtype))
         g.replay()
         torch.cuda.synchronize()
         got = out.clone()
@@ -162,7 +179,7 @@ def test_graph_replays_of_the_shared_prefix_pass_match_eager():
         torch.cuda.synchronize()
         assert torch.isfinite(got.float()).all()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
-        r, want = view.expect(q=q)
+        r, want = view.expect(q=q, k=k, v=v)
         assert_close(got.cpu()[r], want, f"shared prefix replay {i}")
         _ = (q.float() * 2).sum()
 
