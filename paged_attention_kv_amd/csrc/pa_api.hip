@@ -1082,6 +1082,6 @@ int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
-const char* pa_version(void) { return "paged_attention_kv_amd 0.1.0 (gfx950)"; }
+const char* pa_version(void) { return "paged_attention_kv_amd 0.2.0 (gfx950)"; }
 
 }  // extern "C"
