@@ -145,10 +145,11 @@ size_t pa_forward_workspace_bytes(int32_t num_tokens, int32_t num_seqs, int32_t 
  * rows verifying a few speculated tokens) every row takes the decode path
  * (either schedule, chosen as for single-token rows), its q_len * G query
  * columns sharing each K/V block, and no prefill launch is made. A batch
- * that makes a prefill launch and has no row longer than 128 keys (by
- * max_seq_len_hint, else max_blocks_per_seq * 16) runs its single-token rows
- * on the prefill path too, so no decode launch is made, unless a flag of
- * pa_forward_ex names the decode schedule.
+ * of at most 256 (row, KV head) pairs that makes a prefill launch and has
+ * no row longer than 128 keys (by max_seq_len_hint, else
+ * max_blocks_per_seq * 16) runs its single-token rows on the prefill path
+ * too, so no decode launch is made, unless a flag of pa_forward_ex names
+ * the decode schedule.
  * Output is fp32-accumulated and rounded to bf16 (round to nearest even).
  * Tuning overrides, read once per process (for sweeps; out-of-range values
  * are ignored): PA_DECODE_STREAM (0 / 1 = always the partitioned / the

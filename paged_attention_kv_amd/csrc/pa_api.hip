@@ -206,6 +206,7 @@ bool mixed_overlap_enabled() {
   static const int v = env_int("PA_MIXED_OVERLAP", 0, 1, 1);
   return v == 1;
 }
+constexpr int64_t kShortBatchMaxTasks = 256;
 bool short_batch_tiles_enabled() {
   static const int v = env_int("PA_SHORT_BATCH_TILES", 0, 1, 1);
   return v == 1;
@@ -562,12 +563,18 @@ int forward_impl(const WriteArgs* wr, const void* q, const void* k_cache, const 
   // call returns; not under graph capture, and not for the no-allocation
   // entry point (the side stream is made on first use).
   const bool has_prefill = a.max_query_len > w.qmax;
-  // A batch with prefill rows in which no row is longer than the few-key
-  // tiles' bound (list A stays empty) runs every row, the single-token ones
-  // too, as few-key tiles: the planner and one tile launch, no decode launch.
-  // Not when a flag names the decode schedule; PA_SHORT_BATCH_TILES=0 turns
-  // it off (for comparisons).
+  // A small batch with prefill rows in which no row is longer than the
+  // few-key tiles' bound (list A stays empty) runs every row, the
+  // single-token ones too, as few-key tiles: the planner and one tile
+  // launch, no decode launch. Small: at most kShortBatchMaxTasks (row, KV
+  // head) pairs, one tile task per workgroup of the few-key grid; with more,
+  // each decode row's tile costs more than the decode launch saves (the
+  // decode launch and the tiles against all rows as tiles, D 128 and 8 KV
+  // heads: 16 rows 19.5 against 15.0 us, 64 rows 22.3 against 23.0, 256
+  // rows 38.1 against 61.5). Not when a flag names the decode schedule;
+  // PA_SHORT_BATCH_TILES=0 turns it off (for comparisons).
   const bool all_rows = has_prefill && a.max_seq_len <= pa::prefill_split_keys() &&
+                        (int64_t)num_seqs * num_kv_heads <= kShortBatchMaxTasks &&
                         !(flags &
                           (PA_FORWARD_DECODE_EVEN_SHARES | PA_FORWARD_DECODE_PARTITIONED)) &&
                         short_batch_tiles_enabled();

@@ -494,7 +494,7 @@ def test_sweep_short_batch_all_rows_as_tiles(d, hq, hkv):
     """Batches whose rows are all at most 128 keys long, mixing single-token
     rows with chunks: every row runs as a few-key tile (no decode launch),
     each group size and head size against the oracle."""
-    r = random.Random(hash(("short", d, hq, hkv)) % 1000)
+    r = random.Random(1000 + 7 * d + 131 * hq + hkv)
     rows = []
     for _ in range(12):
         ql = r.choice([0, 1, 1, 1, 2, 5, 16, 17, 33, 100])
@@ -835,10 +835,11 @@ def test_short_rows_launch_no_long_tile_list(hinted, schedule):
 
 
 def test_short_batch_of_decode_rows_as_tiles_matches_the_decode_launch():
-    """Many single-token rows of at most 128 keys beside one prompt: the
-    few-key tiles that take them (no decode launch) match the oracle on
-    every row and the decode launch (a schedule flag) to the bar."""
-    rows = [(1, (29 * i) % 128) for i in range(300)] + [(64, 60)]
+    """31 single-token rows of at most 128 keys beside one prompt (256 (row,
+    KV head) pairs): the few-key tiles that take them (no decode launch)
+    match the oracle on every row and the decode launch (a schedule flag)
+    to the bar."""
+    rows = [(1, (29 * i) % 128) for i in range(31)] + [(64, 60)]
     spec = wl.custom("short_decode", 32, 8, 128, rows=rows, seed=95, max_blocks_per_seq=8)
     case = wl.make_case(spec, device=DEV)
     view = OracleView(case, range(spec.num_seqs))
@@ -850,6 +851,22 @@ def test_short_batch_of_decode_rows_as_tiles_matches_the_decode_launch():
     assert_close(tiles.cpu()[r], want, "decode rows as tiles")
     dec = write_and_forward(case, decode_schedule="partitioned")
     assert_close(tiles.cpu().float(), dec.cpu().float(), "tiles against the decode launch")
+
+
+def test_large_short_batch_keeps_the_decode_launch():
+    """Past 256 (row, KV head) pairs a batch of short rows keeps its
+    single-token rows on the decode launch (tiles cost more there); every
+    row against the oracle."""
+    rows = [(1, 8 + (29 * i) % 120) for i in range(300)] + [(64, 60)]
+    spec = wl.custom("short_many", 32, 8, 128, rows=rows, seed=96, max_blocks_per_seq=8)
+    case = wl.make_case(spec, device=DEV)
+    view = OracleView(case, range(spec.num_seqs))
+    pa.profile_begin()
+    out = fused_call(case, max_query_len=64).clone()
+    per = pa.profile_end()
+    assert per["decode"][0] == 1 and per["prefill_short"][0] == 1, per
+    r, want = view.expect()
+    assert_close(out.cpu()[r], want, "many short rows")
 
 
 def test_nan_poison_outside_context_does_not_leak():
