@@ -387,6 +387,22 @@ int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
                        int32_t max_query_len_hint, int32_t max_seq_len_hint, void* stream);
 
 /*
+ * Synchronous check of the shared-prefix calls' caller contract (section
+ * "Prefix Caching": a cached block is shared by reference, only full blocks
+ * are shared, and a request's new tokens go into blocks of its own), for
+ * tests and debugging; copies to the host and waits on `stream`. Checks:
+ * every row's first prefix_blocks table entries equal row 0's; every row's
+ * seq_len is above 16 * prefix_blocks and at most max_blocks_per_seq * 16;
+ * and, if slot_mapping (int64 [num_seqs], one new token per row) is not
+ * NULL, no slot >= 0 lies in one of the prefix's blocks. Returns PA_OK or
+ * PA_ERR_INVALID_DATA (or an argument error); pa_last_error() names the
+ * first row that breaks the contract.
+ */
+int pa_validate_shared_prefix(const int32_t* block_table, const int32_t* seq_lens,
+                              const int64_t* slot_mapping, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int32_t prefix_blocks, void* stream);
+
+/*
  * Read probe for measurement harnesses (not part of the attention path):
  * reads every K and V block that rows 0..num_seqs-1 cover (the first
  * ceil(seq_lens[s] / 16) entries of each table row, the blocks a forward

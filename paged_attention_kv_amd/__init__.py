@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["cache_write", "forward", "write_and_forward", "write_and_forward_noalloc",
            "forward_shared_prefix", "write_and_forward_shared_prefix",
-           "forward_workspace_bytes",
+           "validate_shared_prefix", "forward_workspace_bytes",
            "validate_inputs",
            "kv_block_bytes", "last_error", "version", "library_path", "load_library",
            "profile_begin", "profile_end", "PaError", "BLOCK_SIZE", "KERNEL_CLASSES"]
@@ -91,6 +91,7 @@ SIGNATURES = {
                                                     ctypes.c_uint32, _P]),
     "pa_validate_inputs": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32,
                                           _I32, _I32, _P]),
+    "pa_validate_shared_prefix": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P]),
     "pa_probe_block_read": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32,
                                            _I32, _P, _P]),
     "pa_profile_begin": (ctypes.c_int, []),
@@ -510,6 +511,28 @@ def validate_inputs(block_table: torch.Tensor, seq_lens: torch.Tensor,
                                   num_tokens, S, MB, num_blocks, BLOCK_SIZE, nw,
                                   max_query_len or 0, max_seq_len or 0,
                                   _stream(block_table)))
+
+
+def validate_shared_prefix(block_table: torch.Tensor, seq_lens: torch.Tensor, prefix_blocks: int,
+                           slot_mapping: Optional[torch.Tensor] = None) -> None:
+    """Synchronously check the shared-prefix calls' caller contract (every
+    row's first ``prefix_blocks`` table entries equal row 0's, every row
+    longer than the prefix, no new token's slot in a prefix block); raises
+    PaError(PA_ERR_INVALID_DATA) naming the first row that breaks it."""
+    lib = load_library()
+    _dev_tensor("block_table", block_table, torch.int32, 2)
+    _dev_tensor("seq_lens", seq_lens, torch.int32, 1)
+    S, MB = block_table.shape
+    if seq_lens.shape[0] != S:
+        raise ValueError("seq_lens must have one entry per table row")
+    if slot_mapping is not None:
+        _dev_tensor("slot_mapping", slot_mapping, torch.int64, 1)
+        if slot_mapping.shape[0] != S:
+            raise ValueError("slot_mapping must hold one new token per row")
+    _check(lib.pa_validate_shared_prefix(
+        block_table.data_ptr(), seq_lens.data_ptr(),
+        None if slot_mapping is None else slot_mapping.data_ptr(), S, MB, prefix_blocks,
+        _stream(block_table)))
 
 
 def probe_block_read(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

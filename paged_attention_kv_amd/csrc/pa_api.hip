@@ -1087,6 +1087,43 @@ int pa_validate_inputs(const int32_t* block_table, const int32_t* seq_lens,
   return PA_OK;
 }
 
+int pa_validate_shared_prefix(const int32_t* block_table, const int32_t* seq_lens,
+                              const int64_t* slot_mapping, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int32_t prefix_blocks, void* stream) {
+  g_last_error.clear();
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_blocks_per_seq > kMaxBlocksPerSeq ||
+      prefix_blocks <= 0 || prefix_blocks >= max_blocks_per_seq)
+    return fail(PA_ERR_SHAPE, "pa_validate_shared_prefix: a size is out of range");
+  if (!block_table || !seq_lens)
+    return fail(PA_ERR_NULL, "pa_validate_shared_prefix: null pointer argument");
+  if (num_seqs == 0) return PA_OK;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pa_validate_shared_prefix sync");
+  std::vector<int32_t> lens(num_seqs), table((size_t)num_seqs * max_blocks_per_seq);
+  std::vector<int64_t> slots(slot_mapping ? num_seqs : 0);
+  if ((e = hipMemcpy(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost)) ||
+      (e = hipMemcpy(table.data(), block_table, table.size() * 4, hipMemcpyDeviceToHost)) ||
+      (slot_mapping &&
+       (e = hipMemcpy(slots.data(), slot_mapping, slots.size() * 8, hipMemcpyDeviceToHost))))
+    return hip_fail(e, "pa_validate_shared_prefix copy");
+  const int64_t prefix_keys = (int64_t)prefix_blocks * PA_BLOCK_SIZE;
+  const int64_t cap = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+  std::unordered_set<int64_t> prefix(table.begin(), table.begin() + prefix_blocks);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (lens[s] <= prefix_keys || lens[s] > cap)
+      return fail(PA_ERR_INVALID_DATA, "sequence %d: seq_len %d outside (%lld, %lld]", s,
+                  lens[s], (long long)prefix_keys, (long long)cap);
+    for (int32_t b = 0; b < prefix_blocks; ++b)
+      if (table[(size_t)s * max_blocks_per_seq + b] != table[b])
+        return fail(PA_ERR_INVALID_DATA, "sequence %d: block_table[%d] = %d, row 0 has %d", s,
+                    b, table[(size_t)s * max_blocks_per_seq + b], table[b]);
+    if (slot_mapping && slots[s] >= 0 && prefix.count(slots[s] / PA_BLOCK_SIZE))
+      return fail(PA_ERR_INVALID_DATA, "sequence %d: slot %lld lies in a prefix block", s,
+                  (long long)slots[s]);
+  }
+  return PA_OK;
+}
+
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
 const char* pa_version(void) { return "paged_attention_kv_amd 0.2.0 (gfx950)"; }

@@ -217,6 +217,17 @@ def test_shared_prefix_calls_reject_bad_arguments(lib):
     assert sp(True, k=NULL, S=0) == 0         # nothing to write
 
 
+def test_validate_shared_prefix_rejects_bad_arguments_before_touching_the_device(lib):
+    v = lib.pa_validate_shared_prefix
+    assert v(None, FAKE, None, 4, 8, 2, None) == -1
+    assert v(FAKE, None, None, 4, 8, 2, None) == -1
+    assert v(FAKE, FAKE, None, 4, 8, 0, None) == -2     # no prefix
+    assert v(FAKE, FAKE, None, 4, 8, 8, None) == -2     # prefix covers the table
+    assert v(FAKE, FAKE, None, -1, 8, 2, None) == -2
+    assert v(FAKE, FAKE, None, 4, 1 << 27, 2, None) == -2
+    assert v(FAKE, FAKE, None, 0, 8, 2, None) == 0       # no rows: nothing to check
+
+
 def test_header_constants_match_the_binding():
     text = open(HEADER).read()
     assert int(re.search(r"#define PA_BLOCK_SIZE (\d+)", text).group(1)) == pa.BLOCK_SIZE

@@ -442,6 +442,30 @@ def test_write_and_forward_shared_prefix_skips_negative_slots():
     assert_close(one.cpu()[r], want, "shared prefix rows with slots")
 
 
+def test_validate_shared_prefix_names_the_first_broken_row():
+    """pa_validate_shared_prefix accepts a well-formed prefix-shared batch
+    and names the first row that breaks the contract: a table entry of the
+    prefix that differs from row 0's, a row no longer than the prefix, a
+    new token's slot in a prefix block."""
+    pb = 3
+    rows = [(1, 16 * pb + n - 1) for n in (5, 17, 1, 40)]
+    spec = wl.custom("sp_validate", 32, 8, 128, rows=rows, seed=132, shared_prefix_blocks=pb)
+    case = wl.make_case(spec, device=DEV)
+    pa.validate_shared_prefix(case.block_table, case.seq_lens, pb, case.slot_mapping)
+    table = case.block_table.clone()
+    table[2, 1] = table[0, 1] + 1
+    with pytest.raises(pa.PaError, match="sequence 2"):
+        pa.validate_shared_prefix(table, case.seq_lens, pb)
+    lens = case.seq_lens.clone()
+    lens[3] = 16 * pb
+    with pytest.raises(pa.PaError, match="sequence 3"):
+        pa.validate_shared_prefix(case.block_table, lens, pb)
+    slots = case.slot_mapping.clone()
+    slots[1] = int(case.block_table[0, 2]) * 16 + 5
+    with pytest.raises(pa.PaError, match="sequence 1"):
+        pa.validate_shared_prefix(case.block_table, case.seq_lens, pb, slots)
+
+
 def test_shared_prefix_rejects_bad_arguments():
     spec = wl.custom("sp_bad", 32, 8, 128, rows=[(1, 40), (1, 50)], seed=130,
                      shared_prefix_blocks=2)
