@@ -112,6 +112,21 @@ int32_t pa_sched_request_computed(const pa_sched* s, int64_t request_id);
 /* Reference count of a block (-1 if out of range). */
 int32_t pa_sched_block_ref_count(const pa_sched* s, int32_t block);
 
+/*
+ * Leading blocks that every row of a planned step shares (host arrays as
+ * pa_sched_step_inputs fills them; section "Prefix Caching": requests with
+ * the same prompt prefix reference the same full blocks): the largest P
+ * such that every row's first P table entries equal row 0's and every row
+ * keeps at least one key past 16 * P, so that its new token lies in a block
+ * of its own. 0 when a row does not hold exactly one query token (the
+ * shared-prefix calls take decode rows only) or on bad arguments. The
+ * shared-prefix calls (pa_write_and_forward_shared_prefix) apply to the
+ * step when it is above 0.
+ */
+int32_t pa_sched_shared_prefix_blocks(const int32_t* query_start_loc, const int32_t* seq_lens,
+                                      const int32_t* block_table, int32_t num_seqs,
+                                      int32_t table_cols);
+
 #ifdef __cplusplus
 }  // extern "C"
 #endif

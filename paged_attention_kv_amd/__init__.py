@@ -66,6 +66,7 @@ SIGNATURES = {
     "pa_sched_request_blocks": (_I32, [_P, _I64, _P, _I32]),
     "pa_sched_request_computed": (_I32, [_P, _I64]),
     "pa_sched_block_ref_count": (_I32, [_P, _I32]),
+    "pa_sched_shared_prefix_blocks": (_I32, [_P, _P, _P, _I32, _I32]),
     "pa_kv_block_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "pa_cache_write": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _P]),
     "pa_forward_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),

@@ -462,4 +462,25 @@ int32_t pa_sched_block_ref_count(const pa_sched* s, int32_t block) {
   return s->pool.at(block).ref;
 }
 
+int32_t pa_sched_shared_prefix_blocks(const int32_t* query_start_loc, const int32_t* seq_lens,
+                                      const int32_t* block_table, int32_t num_seqs,
+                                      int32_t table_cols) {
+  if (!query_start_loc || !seq_lens || !block_table || num_seqs <= 0 || table_cols <= 0)
+    return 0;
+  // every row a decode row; the prefix ends a key before the shortest row
+  int64_t p = table_cols;
+  for (int32_t r = 0; r < num_seqs; ++r) {
+    if (query_start_loc[r + 1] - query_start_loc[r] != 1 || seq_lens[r] < 1) return 0;
+    p = std::min<int64_t>(p, (seq_lens[r] - 1) / PA_BLOCK_SIZE);
+  }
+  // the leading entries every row shares with row 0
+  for (int32_t r = 1; r < num_seqs && p > 0; ++r) {
+    const int32_t* row = block_table + (size_t)r * table_cols;
+    int64_t b = 0;
+    while (b < p && row[b] == block_table[b]) ++b;
+    p = b;
+  }
+  return (int32_t)p;
+}
+
 }  // extern "C"

@@ -31,6 +31,18 @@ class StepInputs:
     def num_tokens(self) -> int:
         return int(self.slot_mapping.shape[0])
 
+    def shared_prefix_blocks(self) -> int:
+        """Leading blocks every row shares, when every row is a decode row
+        (pa_sched_shared_prefix_blocks); above 0, the step can take the
+        shared-prefix calls."""
+        if self.num_seqs == 0:
+            return 0
+        qsl = np.ascontiguousarray(self.query_start_loc, dtype=np.int32)
+        lens = np.ascontiguousarray(self.seq_lens, dtype=np.int32)
+        table = np.ascontiguousarray(self.block_table, dtype=np.int32)
+        return int(load_library().pa_sched_shared_prefix_blocks(
+            _ptr(qsl), _ptr(lens), _ptr(table), self.num_seqs, table.shape[1]))
+
 
 def _ptr(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)

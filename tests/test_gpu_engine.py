@@ -1,5 +1,7 @@
 """End to end on the GPU: the native step planner (block pool, prefix cache,
-chunked prefill, preemption) feeds pa_write_and_forward step after step.
+chunked prefill, preemption) feeds pa_write_and_forward step after step (and
+pa_write_and_forward_shared_prefix on steps whose decode rows share a
+cached prefix).
 
 Every token's K, V and q are a fixed function of the tokens up to it (as in
 a causal model), so a block reused from the prefix cache holds exactly the
@@ -56,7 +58,8 @@ class Mirror:
 
 
 def run_engine(Hq, Hkv, D, num_blocks, budget, threshold, caching, seed, n_req=12,
-               new_tokens=(2, 10)):
+               new_tokens=(2, 10), one_prefix=False, shared_prefix_calls=False,
+               first_alone_steps=0):
     rng = random.Random(seed)
     sch = Scheduler(num_blocks, max_num_batched_tokens=budget, max_num_seqs=8,
                     long_prefill_token_threshold=threshold, enable_prefix_caching=caching)
@@ -64,18 +67,19 @@ def run_engine(Hq, Hkv, D, num_blocks, budget, threshold, caching, seed, n_req=1
     prefixes = [[rng.randrange(30_000) for _ in range(BS * rng.randrange(2, 4))] for _ in range(2)]
     pending = []
     for r in range(n_req):
-        p = (rng.choice(prefixes) if rng.random() < 0.7 else []) + \
-            [rng.randrange(30_000) for _ in range(rng.randrange(3, 50))]
+        head = prefixes[0] if one_prefix else (rng.choice(prefixes) if rng.random() < 0.7 else [])
+        p = head + [rng.randrange(30_000) for _ in range(rng.randrange(3, 50))]
         pending.append((r, p, rng.randrange(*new_tokens)))
     k_cache = torch.full((num_blocks, BS, Hkv, D), float("nan"), dtype=torch.bfloat16, device=DEV)
     v_cache = torch.full_like(k_cache, float("nan"))
     scale = D ** -0.5
     MB = num_blocks
     live = set()
-    steps = checked_rows = 0
+    steps = checked_rows = shared_steps = 0
     while pending or live:
         # requests arrive over the first steps
-        while pending and (steps % 2 == 0 or not live):
+        while pending and (steps % 2 == 0 or not live) and \
+                (steps >= first_alone_steps or not live):
             r, p, m = pending.pop(0)
             sch.add_request(r, p, m)
             mir.add(r, p)
@@ -98,9 +102,19 @@ def run_engine(Hq, Hkv, D, num_blocks, budget, threshold, caching, seed, n_req=1
         table = dev(inp.block_table, torch.int32)
         slots = dev(inp.slot_mapping, torch.int64)
         ql = np.diff(inp.query_start_loc)
-        out = pa.write_and_forward(k.to(DEV), v.to(DEV), slots, k_cache, v_cache, q.to(DEV),
-                                   table, lens, qsl, scale, max_query_len=int(ql.max()),
-                                   max_seq_len=int(inp.seq_lens.max()))
+        pb = inp.shared_prefix_blocks() if shared_prefix_calls else 0
+        if pb > 0:
+            # every row decodes and shares the leading pb blocks: the prefix
+            # is attended once for all rows, the write in the same launch
+            out = pa.write_and_forward_shared_prefix(k.to(DEV), v.to(DEV), slots, k_cache,
+                                                     v_cache, q.to(DEV), table, lens, qsl,
+                                                     scale, pb,
+                                                     max_seq_len=int(inp.seq_lens.max()))
+            shared_steps += 1
+        else:
+            out = pa.write_and_forward(k.to(DEV), v.to(DEV), slots, k_cache, v_cache, q.to(DEV),
+                                       table, lens, qsl, scale, max_query_len=int(ql.max()),
+                                       max_seq_len=int(inp.seq_lens.max()))
         torch.cuda.synchronize()
         out = out.cpu()
         kc, vc = k_cache.cpu(), v_cache.cpu()
@@ -147,8 +161,10 @@ def run_engine(Hq, Hkv, D, num_blocks, budget, threshold, caching, seed, n_req=1
         assert steps < 2000
     st = sch.stats()
     print(f"\n  steps {steps}, rows checked {checked_rows}, prefix hits {st.prefix_hit_tokens} "
-          f"tokens, preemptions {st.num_preemptions}", flush=True)
+          f"tokens, preemptions {st.num_preemptions}, shared-prefix steps {shared_steps}",
+          flush=True)
     assert st.num_finished == n_req and st.num_free_blocks == num_blocks
+    st.shared_prefix_steps = shared_steps
     return st
 
 
@@ -156,6 +172,19 @@ def run_engine(Hq, Hkv, D, num_blocks, budget, threshold, caching, seed, n_req=1
 def test_engine_steps_with_prefix_cache_and_chunked_prefill(Hq, Hkv, D):
     st = run_engine(Hq, Hkv, D, num_blocks=96, budget=80, threshold=24, caching=True, seed=D)
     assert st.prefix_hit_tokens > 0
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 64), (32, 8, 128)])
+def test_engine_decode_steps_through_the_shared_prefix_call(Hq, Hkv, D):
+    """Every request starts with the same prompt prefix: the planner's
+    steps whose rows all decode and share its cached blocks go through
+    pa_write_and_forward_shared_prefix, and every row still matches the
+    oracle and every cache row its token's K/V."""
+    # the first request computes the prefix alone; the others find it cached
+    st = run_engine(Hq, Hkv, D, num_blocks=96, budget=80, threshold=24, caching=True,
+                    seed=31 + D, n_req=8, new_tokens=(24, 32), one_prefix=True,
+                    shared_prefix_calls=True, first_alone_steps=6)
+    assert st.prefix_hit_tokens > 0 and st.shared_prefix_steps >= 5
 
 
 def test_engine_steps_under_preemption():

@@ -226,3 +226,51 @@ def test_argument_errors():
     sch.schedule()
     with pytest.raises(pa.PaError):
         sch.schedule()                        # the planned step was not updated
+
+
+def test_shared_prefix_blocks_of_a_step():
+    """pa_sched_shared_prefix_blocks on hand-made step inputs: the leading
+    table entries every row shares with row 0, capped so every row keeps a
+    key past the prefix, 0 when a row holds other than one query token."""
+    from paged_attention_kv_amd.sched import StepInputs
+    z = np.zeros(0, np.int64)
+
+    def step(qls, lens, table):
+        qsl = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+        return StepInputs(np.arange(len(qls), dtype=np.int64), qsl, np.array(lens, np.int32),
+                          np.array(table, np.int32), z, z.astype(np.int32), z.astype(np.int32))
+
+    t = [[5, 6, 7, 8, 0], [5, 6, 7, 9, 1], [5, 6, 7, 8, 2]]
+    assert step([1, 1, 1], [70, 70, 70], t).shared_prefix_blocks() == 3
+    assert step([1, 1, 1], [70, 48, 70], t).shared_prefix_blocks() == 2   # row 1: 48 keys
+    assert step([1, 1, 1], [70, 49, 70], t).shared_prefix_blocks() == 3
+    assert step([1, 2, 1], [70, 70, 70], t).shared_prefix_blocks() == 0   # not decode rows
+    assert step([1, 0, 1], [70, 70, 70], t).shared_prefix_blocks() == 0
+    t2 = [[5, 6, 7], [4, 6, 7]]
+    assert step([1, 1], [40, 40], t2).shared_prefix_blocks() == 0       # first blocks differ
+    assert step([1], [40], [[5, 6, 7]]).shared_prefix_blocks() == 2      # one row: its own
+    lib = pa.load_library()
+    assert lib.pa_sched_shared_prefix_blocks(None, None, None, 3, 5) == 0
+
+
+def test_decode_steps_of_requests_with_a_cached_prompt_share_its_blocks():
+    """Requests whose prompts start with the same 3 full blocks: once every
+    row decodes, the planned step's rows share those blocks (prefix caching
+    hands the same blocks to each), and the shared-prefix count says so."""
+    prefix = list(range(2000, 2000 + 3 * BS))
+    sch = Scheduler(64, max_num_batched_tokens=512)
+    # the first request computes the prefix; the others, admitted after,
+    # find its blocks in the cache
+    sch.add_request(0, prefix + [0, 1, 2], max_new_tokens=6)
+    counts = []
+    for step in range(5):
+        if step == 1:
+            for r in range(1, 4):
+                sch.add_request(r, prefix + [r, r + 1, 2 * r + 2], max_new_tokens=4)
+        inp = sch.schedule(table_cols=8)
+        check_step(sch, inp)
+        counts.append(inp.shared_prefix_blocks())
+        sch.update([7] * inp.num_seqs)
+    # prompt step, a step with the others' prompts beside request 0's
+    # decode row, then decode steps of all four
+    assert counts[:2] == [0, 0] and counts[2:] == [3, 3, 3], counts
